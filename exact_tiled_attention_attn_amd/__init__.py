@@ -1,0 +1,16 @@
+"""MI355X-native exact tiled attention forward (bf16, causal / window / GQA).
+
+The compute path is the HIP library ``libattn.so`` built from ``csrc/`` and
+loaded by :mod:`exact_tiled_attention_attn_amd.attn`.  Importing this package
+does not load it; the first use of ``attn_fwd`` (or ``fwd``) does, and fails
+loudly if the library has not been built.
+"""
+
+__all__ = ["attn_fwd", "attn_fwd_ex", "attn_status_string", "fwd", "AttnError"]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import attn as _attn
+        return getattr(_attn, name)
+    raise AttributeError(name)

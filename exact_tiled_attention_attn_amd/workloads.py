@@ -1,0 +1,84 @@
+"""The attention-forward workloads and their algorithmic counts.
+
+Shapes come from the pages:
+
+* 128k context, 32 heads, d = 128 -- "Efficient attention: long context and
+  sub-quadratic variants", section "The quadratic wall, stated concretely".
+* window w = 4096 at N = 131072 -- same page, "Sliding-window and local
+  attention".
+* (2, 32, 8192, 128) causal -- "Efficient Attention: Flash Attention,
+  Sliding Window, Sparse", section "Code".
+* 64 query heads over 8 KV heads -- "Attention Mechanism Variants Beyond
+  Self-Attention", section "Multi-Query and Grouped-Query Attention".
+
+Counting convention: one unmasked score costs 4*d FLOPs (2*d for q.k and 2*d
+for its share of P V), which is the "2N^2 d ... the same again" count of
+"The quadratic wall, stated concretely"; masked or computed-but-discarded
+tile entries never count.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+MI355X_BF16_DENSE_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 bf16 FLOP/CU/clk
+MI355X_HBM_GBPS = 8000.0
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    causal: bool
+    window: int
+    seed: int
+    q_mult: float = 1.0
+    scale: float = field(default=0.0)
+    sampled_rows: int = 0  # 0: the oracle covers every row
+
+    @property
+    def sm_scale(self) -> float:
+        return self.scale if self.scale else 1.0 / math.sqrt(self.d)
+
+
+def visible_scores_per_head(N: int, causal: bool, window: int) -> int:
+    """Number of (i, j) pairs with j visible from i, for one head."""
+    if not causal:
+        return N * N
+    if window <= 0 or window >= N:
+        return N * (N + 1) // 2
+    # rows i < w see i + 1 keys, rows i >= w see exactly w keys
+    return window * (window + 1) // 2 + (N - window) * window
+
+
+def visible_scores(w: Workload) -> int:
+    return w.B * w.Hq * visible_scores_per_head(w.N, w.causal, w.window)
+
+
+def flops(w: Workload) -> int:
+    return 4 * w.d * visible_scores(w)
+
+
+def algorithmic_bytes(w: Workload) -> int:
+    """Q, K, V read once, O (bf16) and lse (fp32) written once."""
+    return 2 * w.B * w.N * w.d * (2 * w.Hq + 2 * w.Hkv) + 4 * w.B * w.Hq * w.N
+
+
+WORKLOADS = {
+    "c1_noncausal_mha": Workload("c1_noncausal_mha", 1, 2, 2, 256, 64, False, 0, 1,
+                                 scale=1.0 / 8.0),
+    "c2_causal_mha": Workload("c2_causal_mha", 2, 32, 32, 8192, 128, True, 0, 2),
+    "c2_causal_mha_sharp": Workload("c2_causal_mha_sharp", 2, 32, 32, 8192, 128, True, 0,
+                                    2, q_mult=4.0),
+    "c3_causal_window": Workload("c3_causal_window", 1, 32, 32, 32768, 128, True, 4096, 3),
+    "c4_causal_gqa": Workload("c4_causal_gqa", 1, 64, 8, 16384, 128, True, 0, 4),
+    "c5_long_causal": Workload("c5_long_causal", 1, 32, 32, 131072, 128, True, 0, 5,
+                               sampled_rows=256),
+    "c5_long_window": Workload("c5_long_window", 1, 32, 32, 131072, 128, True, 4096, 5,
+                               sampled_rows=256),
+}

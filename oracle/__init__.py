@@ -1,0 +1,48 @@
+"""CPU oracle for exact softmax attention forward -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check in the package entry file and the
+``cpu_baseline`` leg of the bench script may import anything in this
+package.  The product path (the HIP library and its Python binding) never
+calls it, and this package never imports the product path: the two share no
+code.  Inputs reach both sides from the seeded generator module, which holds
+none of the attention arithmetic.
+
+Contents
+--------
+``attention``  NumPy float64 implementation of the plain definition, in row
+               blocks restricted to each block's visible key span.
+``brute``      Pure-Python double loops with ``math.fsum``, tiny shapes only;
+               it pins ``attention``.
+
+What the oracle computes (the plain definition; every page agrees that the
+tiled method returns exactly this result):
+
+* "Efficient attention: long context and sub-quadratic variants", section
+  "What it is and when you reach for it": out = softmax(QK^T / sqrt(d)) V.
+* "Efficient Attention: FlashAttention, Sparse, Linear", section 45.2.1
+  (the displayed Attention(Q, K, V) equation).
+* Same first page, section "Implementation, twice": masked entries are set
+  to -inf before the softmax, so they get exactly zero weight and each row
+  renormalises over its visible set; the sliding window lets row i see keys
+  j with i - w < j <= i.
+* "Attention Mechanism Variants Beyond Self-Attention", section
+  "Multi-Query and Grouped-Query Attention": KV heads are repeated with
+  ``repeat_interleave`` so query head h reads KV head h // (Hq / Hkv).
+
+The per-row logsumexp is not defined on any page.  Reading used here: the
+natural-log logsumexp of the *scaled* scores over the row's visible set, so
+that p_ij = exp(s_ij - lse_i).  It is pinned by closed forms (uniform
+weights give ln|V_i|; one-hot retrieval gives ln(e^a + n - 1)) and by
+``torch.logsumexp`` over explicitly masked float64 scores.
+
+Every function here is pinned by tests that do not re-type its formula; no
+function in this package is "parity unpinned".
+"""
+
+from .attention import (  # noqa: F401
+    attention_forward,
+    attention_rows,
+    kv_head_of,
+    visible_span,
+)
+from .brute import brute_attention  # noqa: F401
