@@ -1,0 +1,260 @@
+"""Attention-forward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one attn_fwd call (the whole hot path) over one batch of the
+causal multi-head workload B=2, H=32, N=8192, d=128 (bf16), with Q, K, V
+already resident in HBM.  Throughput counts 4*d FLOPs per unmasked score
+("Efficient attention: long context and sub-quadratic variants", section
+"The quadratic wall, stated concretely"), never the masked entries a tile
+computes and discards.  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (bf16, d=128, causal/window) and % of MFMA peak"
+MAIN = "c2_causal_mha"
+OTHERS = ["c2_causal_mha_sharp", "c3_causal_window", "c4_causal_gqa", "c5_long_causal",
+          "c5_long_window"]
+KERNEL_SRC = os.path.join(ROOT, "exact_tiled_attention_attn_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def device_inputs(w, torch):
+    from exact_tiled_attention_attn_amd.inputs import make_qkv
+    q, k, v = make_qkv(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed)
+    if w.q_mult != 1.0:
+        q = (q.float() * w.q_mult).to(torch.bfloat16)
+    dev = torch.device("cuda:0")
+    return q.to(dev), k.to(dev), v.to(dev), (q, k, v)
+
+
+def time_workload(w, steps, warmup, variant, torch, attn):
+    """Returns (wall ms/step, event ms/launch, host tensors)."""
+    q, k, v, host = device_inputs(w, torch)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        st = attn.attn_fwd_ex(q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.N, w.d, w.sm_scale,
+                              int(w.causal), w.window, variant, stream)
+        if st != 0:
+            raise RuntimeError(f"attn_fwd_ex: {attn.attn_status_string(st)}")
+
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ev_ms = e0.elapsed_time(e1) / steps
+    del q, k, v, o, lse
+    return wall_ms, ev_ms, host
+
+
+def cpu_baseline(w, host, seconds):
+    """The float64 oracle on a bounded sample of the same workload, on the
+    host cores: whole (batch, head) slices' worth of seeded random rows."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from exact_tiled_attention_attn_amd.inputs import sample_rows
+    from oracle import attention_rows
+
+    q, k, v = (t.float().numpy() for t in host)
+    cores = len(os.sched_getaffinity(0))
+    rows = sample_rows(w.N, 1024, seed=w.seed * 7919, edges=())
+
+    def visible(i):
+        hi = i + 1 if w.causal else w.N
+        lo = max(0, i - w.window + 1) if w.window > 0 else 0
+        return hi - lo
+
+    per_slice_scores = sum(visible(int(i)) for i in rows)
+    G = w.Hq // w.Hkv
+    with threadpool_limits(limits=1, user_api="blas"):
+        # calibrate on one slice, then size the sample to about `seconds`
+        t0 = time.perf_counter()
+        attention_rows(q[:1, :1], k[:1, :1], v[:1, :1], w.sm_scale, w.causal, w.window,
+                       rows=rows)
+        one = time.perf_counter() - t0
+        nslices = int(max(1, min(w.B * w.Hq, round(seconds * cores / max(one, 1e-3)))))
+        nslices = max(min(nslices, w.B * w.Hq), 1)
+        heads = list(range(nslices))
+        qs = np.stack([q[h // w.Hq, h % w.Hq] for h in heads])[None]
+        ks = np.stack([k[h // w.Hq, (h % w.Hq) // G] for h in heads])[None]
+        vs = np.stack([v[h // w.Hq, (h % w.Hq) // G] for h in heads])[None]
+        t0 = time.perf_counter()
+        attention_rows(qs, ks, vs, w.sm_scale, w.causal, w.window, rows=rows,
+                       workers=cores)
+        dt = time.perf_counter() - t0
+    flops = 4 * w.d * per_slice_scores * nslices
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{w.name}: {nslices} (batch, head) slices x {len(rows)} seeded random "
+                   f"query rows each ({per_slice_scores * nslices} unmasked scores), float64 "
+                   f"NumPy, one BLAS thread per worker, {cores} workers, {dt:.1f} s"),
+        "seconds": dt,
+        "cpu": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def traffic_for(workload, sha):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get("workloads", {}).get(workload)
+    if not e or t.get("kernel_source_sha") != sha:
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--workload", default=MAIN)
+    ap.add_argument("--no-others", action="store_true", help="time only the main workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from exact_tiled_attention_attn_amd import attn
+    from exact_tiled_attention_attn_amd.workloads import (MI355X_BF16_DENSE_TFLOPS, WORKLOADS,
+                                                          algorithmic_bytes, flops)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    attn.load_library()
+    props = torch.cuda.get_device_properties(0)
+    peak = MI355X_BF16_DENSE_TFLOPS
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    w = WORKLOADS[args.workload]
+    log(f"timing {w.name} variant {args.variant} ({attn.attn_variant_name(args.variant)})")
+    wall_ms, ev_ms, host = time_workload(w, args.steps, args.warmup, args.variant, torch, attn)
+    f = flops(w)
+    value = f / (wall_ms * 1e-3) / 1e12
+    achieved = f / (ev_ms * 1e-3) / 1e12
+    sha = kernel_sha()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: Q, K, V i.i.d. N(0,1) rounded to bf16, seeded",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N,
+                   "d": w.d, "causal": w.causal, "window": w.window,
+                   "variant": attn.attn_variant_name(args.variant)},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic_for(w.name, sha),
+            "kernel": "attn_fwd_kernel",
+            "avg_launch_ms": round(ev_ms, 4),
+            "flops_per_launch": f,
+            "algorithmic_bytes_per_launch": algorithmic_bytes(w),
+        },
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "arch": getattr(props, "gcnArchName", "")},
+        "kernel_source_sha": sha,
+    }
+    if not args.no_others:
+        others = {}
+        for name in OTHERS:
+            ow = WORKLOADS[name]
+            log(f"timing {name}")
+            steps = max(3, args.steps // 4) if ow.N >= 131072 else args.steps
+            wm, em, _ = time_workload(ow, steps, max(1, args.warmup // 2), args.variant, torch,
+                                      attn)
+            of = flops(ow)
+            others[name] = {"tflops": round(of / (em * 1e-3) / 1e12, 2),
+                            "pct_of_peak": round(100 * of / (em * 1e-3) / 1e12 / peak, 2),
+                            "ms": round(em, 4), "steps": steps}
+            torch.cuda.empty_cache()
+        out["other_workloads"] = others
+    if not args.no_cpu:
+        log(f"oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
+        out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

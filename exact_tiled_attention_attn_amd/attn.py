@@ -1,0 +1,153 @@
+"""Python binding of libattn.so (ctypes).  Argument marshalling only.
+
+The names mirror include/attn.h.  Every step of the attention forward runs in
+the HIP library; PyTorch is used here for device memory and the current
+stream.  There is no fallback: if the library is missing or a call fails, an
+``AttnError`` is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn.so")
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = 1
+ATTN_ERR_UNSUPPORTED = 2
+ATTN_ERR_LAUNCH = 3
+ATTN_MAX_N = 1 << 22
+
+EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_num_variants", "attn_variant_name",
+            "attn_status_string", "attn_abi_version")
+
+
+class AttnError(RuntimeError):
+    """The library is missing or returned a non-OK status."""
+
+    def __init__(self, msg, status=None):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def load_library():
+    """Load libattn.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise AttnError(f"{LIB_PATH} is not built; run "
+                        "`python -m exact_tiled_attention_attn_amd.build` first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    lib.attn_fwd.restype = i
+    lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
+    lib.attn_fwd_ex.restype = i
+    lib.attn_num_variants.argtypes = []
+    lib.attn_num_variants.restype = i
+    lib.attn_variant_name.argtypes = [i]
+    lib.attn_variant_name.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [i]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_abi_version.argtypes = []
+    lib.attn_abi_version.restype = i
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x or None
+    return x.data_ptr() or None
+
+
+def _stream(stream, *tensors):
+    if stream is None:
+        if any(getattr(t, "is_cuda", False) for t in tensors):
+            import torch
+            return torch.cuda.current_stream().cuda_stream or None
+        return None
+    if isinstance(stream, int):
+        return stream or None
+    return stream.cuda_stream or None
+
+
+def attn_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, window, stream=None):
+    """Call the C entry point; returns its status code (0 = ATTN_OK).
+
+    q, k, v, o, lse: torch tensors or raw device addresses (int).
+    stream: torch stream, raw hipStream_t (int) or None for the current
+    torch stream.
+    """
+    lib = load_library()
+    return lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(Hq),
+                        int(Hkv), int(N), int(d), float(scale), int(causal), int(window),
+                        _stream(stream, q, k, v, o, lse))
+
+
+def attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, window, variant,
+                stream=None):
+    """attn_fwd with an explicit kernel variant id; returns the status code."""
+    lib = load_library()
+    return lib.attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(Hq),
+                           int(Hkv), int(N), int(d), float(scale), int(causal), int(window),
+                           int(variant), _stream(stream, q, k, v, o, lse))
+
+
+def attn_num_variants():
+    return load_library().attn_num_variants()
+
+
+def attn_variant_name(variant):
+    return load_library().attn_variant_name(int(variant)).decode()
+
+
+def attn_status_string(status):
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def attn_abi_version():
+    return load_library().attn_abi_version()
+
+
+def fwd(q, k, v, causal=False, window=0, scale=None, variant=0, out=None, stream=None):
+    """Allocate (o, lse) with torch and run the forward; raises on any error.
+
+    q: (B, Hq, N, d) bf16 CUDA tensor, contiguous; k, v: (B, Hkv, N, d).
+    Returns o (B, Hq, N, d) bf16 and lse (B, Hq, N) fp32.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise AttnError(f"{name} must be a CUDA (HIP) tensor")
+        if t.dtype != torch.bfloat16:
+            raise AttnError(f"{name} must be bfloat16")
+        if not t.is_contiguous():
+            raise AttnError(f"{name} must be contiguous")
+        if t.dim() != 4:
+            raise AttnError(f"{name} must be (B, H, N, d)")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != tuple(k.shape):
+        raise AttnError("k and v must be (B, Hkv, N, d) matching q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    st = attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, int(bool(causal)), int(window),
+                     variant, stream)
+    if st != ATTN_OK:
+        raise AttnError(f"attn_fwd failed: {attn_status_string(st)} (status {st})", st)
+    return o, lse

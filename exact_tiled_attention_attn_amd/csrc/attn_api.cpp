@@ -1,0 +1,84 @@
+// C ABI entry points: argument validation, then one kernel launch.
+//
+// Validation runs before any HIP call, so a rejected call launches nothing
+// and leaves o / lse untouched.  The rules follow the problem statement in
+// include/attn.h: the visibility rule j <= i (causal) and i - w < j (window)
+// of "Efficient attention: long context and sub-quadratic variants"
+// (sections "Sliding-window and local attention", "Implementation, twice"),
+// where the window is only defined together with the causal mask, and the
+// KV-head map h / (Hq / Hkv) of "Attention Mechanism Variants Beyond
+// Self-Attention" (section "Multi-Query and Grouped-Query Attention"), whose
+// integer head ratio needs Hq to be a multiple of Hkv.
+
+#include <cmath>
+#include <cstdint>
+
+#include "attn.h"
+#include "attn_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+attn_status_t validate(const attn::FwdProblem &p, int variant) {
+  if (variant < 0 || variant >= attn::kNumVariants) return ATTN_ERR_INVALID_ARG;
+  if (p.B < 0 || p.N < 0) return ATTN_ERR_INVALID_ARG;
+  if (p.Hq < 1 || p.Hkv < 1 || p.Hq % p.Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (p.causal != 0 && p.causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(p.scale)) return ATTN_ERR_INVALID_ARG;
+  if (p.d != 64 && p.d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (p.window > 0 && p.causal == 0) return ATTN_ERR_UNSUPPORTED;
+  if (p.N > ATTN_MAX_N) return ATTN_ERR_UNSUPPORTED;
+  if (p.B == 0 || p.N == 0) return ATTN_OK;  // empty problem: pointers unused
+  if (!p.q || !p.k || !p.v || !p.o || !p.lse) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(p.q) || !aligned16(p.k) || !aligned16(p.v) || !aligned16(p.o) ||
+      !aligned16(p.lse))
+    return ATTN_ERR_UNSUPPORTED;
+  // Grid size: B * Hq * ceil(N / 32) workgroup-rows must fit a 32-bit grid.
+  const int64_t rows = static_cast<int64_t>(p.B) * p.Hq * ((static_cast<int64_t>(p.N) + 31) / 32);
+  if (rows > (int64_t{1} << 31) - 1) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
+                          int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                          int window, int variant, void *stream) {
+  attn::FwdProblem p{q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, window};
+  const attn_status_t st = validate(p, variant);
+  if (st != ATTN_OK) return st;
+  if (B == 0 || N == 0) return ATTN_OK;
+  if (p.window >= N) p.window = 0;  // a window covering every key is plain causal
+  if (p.window < 0) p.window = 0;
+  const hipError_t e = attn::launch_fwd(p, variant, static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidValue) return ATTN_ERR_UNSUPPORTED;
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status_t attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                       int Hq, int Hkv, int N, int d, float scale, int causal, int window,
+                       void *stream) {
+  return attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, window, attn::kAuto,
+                     stream);
+}
+
+int attn_num_variants(void) { return attn::kNumVariants; }
+
+const char *attn_variant_name(int variant) { return attn::variant_name(variant); }
+
+const char *attn_status_string(attn_status_t status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported problem";
+    case ATTN_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+}  // extern "C"

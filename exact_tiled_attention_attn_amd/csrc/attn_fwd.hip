@@ -1,0 +1,444 @@
+// gfx950 (MI355X, CDNA4) exact tiled attention forward.
+//
+// What is computed: O = softmax(scale * Q K^T) V with masked scores set to
+// -inf before the softmax, plus the per-row natural logsumexp of the scaled
+// scores ("Efficient Attention: FlashAttention, Sparse, Linear", section
+// 45.2.1; "Efficient attention: long context and sub-quadratic variants",
+// sections "Sliding-window and local attention" and "Implementation, twice").
+// How: the score matrix is produced one 64-key tile at a time on chip and
+// folded into a running output with the running (max, sum) softmax of the
+// same page's section "FlashAttention: exact attention, IO-aware"; tiles that
+// no row of a wave can see are never visited ("Against the real libraries":
+// mask structure becomes loop bounds).
+//
+// Mapping onto CDNA4
+// ------------------
+// * One wave owns 32 query rows of one head.  It computes the transposed
+//   score tile S^T = K Q^T (keys x queries) with v_mfma_f32_32x32x16_bf16:
+//   A = K rows from LDS, B = Q^T held in registers for the whole kernel.
+//   In the 32x32 accumulator, lane l holds query column l % 32 and the keys
+//   8*(r/4) + 4*(l/32) + r%4 for r = 0..15, so every softmax row statistic is
+//   lane-local up to one exchange between lane l and lane l ^ 32
+//   (v_permlane32_swap).
+// * The same accumulator registers, rounded to bf16, are directly the B
+//   operand of O^T += V^T P^T (a 16-key k-step takes registers 8t..8t+7,
+//   i.e. keys 16t + 8*(s/4) + 4*(l/32) + s%4 for slot s), so P never leaves
+//   registers.  The matching V^T A operand is read from key-major LDS with
+//   ds_read_b64_tr_b16: in each 16-lane group, lane 4j+c supplies the address
+//   of 4 consecutive d values of key row j and lane i receives the 4 keys of
+//   column i.
+// * K and V tiles go HBM -> LDS with buffer_load ... lds (16 bytes per lane,
+//   no VGPR staging), double-buffered.  The buffer descriptor spans one
+//   (batch, KV-head) slice, so keys past N read as zero.  Inside a row the
+//   16-byte chunks are XOR-swizzled so that both the b128 K reads and the
+//   transposed V reads hit distinct LDS banks.
+// * GQA: the query heads sharing a KV head are packed into one workgroup
+//   (one head per wave), so each K/V tile is loaded once for all of them.
+// * The running max is exact.  When no row of the wave gets a larger max
+//   from a tile (the common case once a row has seen a few tiles), the
+//   rescale of the O accumulator is skipped with one wave-uniform branch.
+//   An exact max keeps the largest weight of every row at exactly 1.0, so
+//   the bf16 rounding of P never touches the dominant term of a sharp row.
+
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <cmath>
+#include <cstdint>
+
+#include "attn_internal.h"
+
+namespace attn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((vector_size(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
+
+constexpr int kBN = 64;              // keys per tile
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kBufferFlags = 0x00020000;  // gfx9 buffer descriptor word 3
+
+struct Params {
+  const uint16_t *q, *k, *v;
+  uint16_t *o;
+  float *lse;
+  int B, Hq, Hkv, N;
+  int G;          // Hq / Hkv
+  int groups;     // Hq / P (head groups, one per workgroup column)
+  int nq;         // query tiles per head group
+  int total;      // workgroups
+  int nkt;        // key tiles = ceil(N / 64)
+  float c;        // |scale| * log2(e), at least FLT_MIN
+  int neg;        // scale < 0: Q is negated on load, exact in bf16
+  int causal;
+  int window;     // 0: none
+};
+
+template <int D>
+struct Geo {
+  static constexpr int kRowB = D * 2;           // bytes per K/V row
+  static constexpr int kCh = kRowB / 16;        // 16-byte chunks per row
+  static constexpr int kTileB = kBN * kRowB;    // bytes per K or V tile
+  static constexpr int kKSteps = D / 16;        // MFMA k-steps of S^T
+  static constexpr int kDB = D / 32;            // 32-wide d blocks of O^T
+};
+
+// Chunk swizzle of LDS row r (see the header comment).  For D = 128, the 16
+// rows read together by a b128 phase get distinct chunk masks, and the 4
+// consecutive rows of a transposed V read get masks differing in bits 2..3.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (r >> 1) & 7;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufferFlags);
+}
+
+// Workgroup id -> logical id.  Consecutive hardware ids are dealt round-robin
+// to the 8 XCDs; this gives XCD x one contiguous range of logical ids, so the
+// workgroups sharing one head's K/V run behind one L2.
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+  const int q = total >> 3, r = total & 7;
+  const int x = id & 7, slot = id >> 3;
+  return x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
+}
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef char __attribute__((address_space(3))) lchar;
+
+// This thread's share of one K or V tile: kLoads 16-byte chunks.  Chunk
+// n covers tile row r = ci / kCh, chunk p = ci % kCh with
+// ci = n * NW * 64 + tid, so each wave instruction reads whole rows
+// contiguously from HBM.  Keys past N read as zero (buffer range check).
+template <int D, int NW>
+struct TileStage {
+  using g = Geo<D>;
+  static constexpr int kLoads = kBN * g::kCh / (NW * 64);
+  static_assert(kLoads * NW * 64 == kBN * g::kCh, "tile must split evenly over the threads");
+  u32x4 k[kLoads], v[kLoads];
+
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int j0,
+                                       int tid) {
+#pragma unroll
+    for (int n = 0; n < kLoads; ++n) {
+      const int ci = n * NW * 64 + tid;
+      const int voff = j0 * g::kRowB + ci * 16;
+      k[n] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff, 0, 0);
+      v[n] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0);
+    }
+  }
+  // Write into an LDS buffer set (K tile, then V tile), chunk p of row r at
+  // position p ^ swz(r).
+  __device__ __forceinline__ void store(lchar *set, int tid) const {
+#pragma unroll
+    for (int n = 0; n < kLoads; ++n) {
+      const int ci = n * NW * 64 + tid;
+      const int r = ci / g::kCh, p = ci % g::kCh;
+      const int off = r * g::kRowB + ((p ^ swz<D>(r)) * 16);
+      *(__attribute__((address_space(3))) u32x4 *)(set + off) = k[n];
+      *(__attribute__((address_space(3))) u32x4 *)(set + g::kTileB + off) = v[n];
+    }
+  }
+};
+
+__device__ __forceinline__ float wave_max_pair(float x) {
+  // max of this lane and lane ^ 32
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float wave_sum_pair(float x) {
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+template <int D, int NW, int P>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
+  using g = Geo<D>;
+  constexpr int kRows = 32 * NW / P;  // query rows per workgroup
+
+  // Two LDS buffer sets, each a K tile followed by a V tile.
+  __shared__ __attribute__((aligned(1024))) char smem[4 * g::kTileB];
+  lchar *const set0 = (lchar *)smem;
+  lchar *const set1 = (lchar *)smem + 2 * g::kTileB;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  // ---- which (batch, head, rows) this workgroup and wave own
+  const int logical = xcd_remap(blockIdx.x, prm.total);
+  const int qrank = logical % prm.nq;
+  const int hgb = logical / prm.nq;
+  const int hg = hgb % prm.groups, b = hgb / prm.groups;
+  const int qi = prm.causal ? (prm.nq - 1 - qrank) : qrank;  // heaviest tiles first
+  const int head = hg * P + (wave % P);
+  const int kvh = __builtin_amdgcn_readfirstlane((hg * P) / prm.G);
+  const int wg_r0 = qi * kRows;
+  const int qw0 = wg_r0 + (wave / P) * 32;  // first row of this wave
+  const int N = prm.N;
+
+  // key-tile ranges: workgroup (union over its rows) and this wave
+  auto tile_range = [&](int r0, int r1, int &lo, int &hi) {  // rows [r0, r1)
+    hi = prm.causal ? min(prm.nkt, (r1 - 1) / kBN + 1) : prm.nkt;
+    lo = prm.window > 0 ? max(0, r0 - prm.window + 1) / kBN : 0;
+  };
+  int wg_lo, wg_hi, w_lo, w_hi;
+  tile_range(wg_r0, min(N, wg_r0 + kRows), wg_lo, wg_hi);
+  if (qw0 < N) {
+    tile_range(qw0, min(N, qw0 + 32), w_lo, w_hi);
+  } else {
+    w_lo = w_hi = 0;  // rows past the end: this wave only helps load tiles
+  }
+
+  // every wave of the workgroup reads the same KV head (P divides G)
+  const size_t kv_slice = (size_t)(b * prm.Hkv + kvh) * N * D;
+  const size_t q_slice = (size_t)(b * prm.Hq + head) * N * D;
+  const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(prm.k + kv_slice, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(prm.v + kv_slice, (uint32_t)N * D * 2);
+
+  // ---- Q^T operand: lane holds query row qw0 + l32, d = 16*kk + 8*hh + s
+  bf16x8 qf[g::kKSteps];
+  {
+    const int row = qw0 + l32;
+    const uint16_t *qp = prm.q + q_slice + (size_t)row * D + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < g::kKSteps; ++kk) {
+      if (row < N) {
+        qf[kk] = *(const bf16x8 *)(qp + 16 * kk);
+      } else {
+        qf[kk] = bf16x8{};
+      }
+      if (prm.neg) {
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 t = __builtin_bit_cast(u32x4, qf[kk]);
+        t ^= 0x80008000u;
+        qf[kk] = __builtin_bit_cast(bf16x8, t);
+      }
+    }
+  }
+
+  // per-lane LDS byte offsets
+  // K (b128): row 32*rb + l32, chunk (2*kk + hh) ^ swz(l32)
+  const int k_row_off = l32 * g::kRowB;
+  const int k_swz = swz<D>(l32);
+  // V (tr read): key row 32rb + 16t + 8u + koff, d = 32db + doff
+  const int v_koff = 4 * hh + ((lane & 15) >> 2);
+  const int v_dgrp = (lane >> 4) & 1;      // which 16-wide half of the 32-d block
+  const int v_c = lane & 3;                // which 4-wide piece of the 16
+  // chunk index (before swizzle) of d = 32db + 16*v_dgrp + 4*v_c is
+  // 4*db + 2*v_dgrp + (v_c >> 1); byte within the chunk 8*(v_c & 1).
+
+  f32x16 oacc[g::kDB];
+#pragma unroll
+  for (int i = 0; i < g::kDB; ++i) oacc[i] = f32x16{};
+  float m2 = -1e30f;   // running max, scaled log2 units (finite: no inf - inf)
+  float lsum = 0.0f;   // this lane's partial row sum (its 32 of every 64 keys)
+  const float c = prm.c;
+
+  TileStage<D, NW> stage;
+  if (wg_lo < wg_hi) {
+    stage.load(rs_k, rs_v, wg_lo * kBN, tid);
+    stage.store(set0, tid);
+  }
+  __syncthreads();
+
+  // S^T, mask, online softmax and O^T update for key tile t held in `set`.
+  auto compute = [&](const int t, const lchar *const set) {
+
+    const int j0 = t * kBN;
+    const lchar *kb = set;
+    const lchar *vb = set + g::kTileB;
+
+    // ---- S^T = K Q^T for 64 keys x 32 queries
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kk = 0; kk < g::kKSteps; ++kk) {
+      const int choff = (((2 * kk + hh) ^ k_swz)) * 16;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const bf16x8 a = *(const lds_bf16x8_t *)(kb + rb * 32 * g::kRowB + k_row_off + choff);
+        s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[rb], 0, 0, 0);
+      }
+    }
+
+    // ---- mask: only tiles that hold a masked (row, key) pair for this wave
+    const bool need_mask = (prm.causal && j0 + kBN - 1 > qw0) ||
+                           (prm.window > 0 && j0 <= qw0 + 31 - prm.window) || (j0 + kBN > N);
+    if (need_mask) {
+      const int qrow = qw0 + l32;
+      const int kbase = j0 + 4 * hh;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kbase + 32 * rb + 8 * (r >> 2) + (r & 3);
+          bool vis = key < N;
+          if (prm.causal) vis = vis && key <= qrow;
+          if (prm.window > 0) vis = vis && key > qrow - prm.window;
+          s[rb][r] = vis ? s[rb][r] : -INFINITY;
+        }
+      }
+    }
+
+    // ---- online softmax (scaled log2 domain)
+    float mx = s[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+    mx = wave_max_pair(mx);
+    const float mt2 = mx * c;
+    const bool grow = mt2 > m2;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float mnew = fmaxf(m2, mt2);
+      const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < g::kDB; ++i) oacc[i] *= alpha;
+      m2 = mnew;
+    }
+    const float negm = -m2;
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][8 * tt + e], c, negm));
+          lsum += p;
+          pf[rb][tt][e] = (__bf16)p;
+        }
+      }
+    }
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < g::kDB; ++db) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          i16x4 half[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int row = 32 * rb + 16 * tt + 8 * u + v_koff;
+            const int chunk = (4 * db + 2 * v_dgrp + (v_c >> 1)) ^ swz<D>(row);
+            const int off = row * g::kRowB + chunk * 16 + 8 * (v_c & 1);
+            half[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vb + off));
+          }
+          typedef short i16x8 __attribute__((ext_vector_type(8)));
+          i16x8 both = {half[0][0], half[0][1], half[0][2], half[0][3],
+                        half[1][0], half[1][1], half[1][2], half[1][3]};
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both),
+                                                             pf[rb][tt], oacc[db], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // One key tile: start loading the next tile into registers, compute this
+  // one from LDS (if this wave sees any of its keys), then park the next tile
+  // in the other buffer set.  The register loads are only waited for at that
+  // final store, so they overlap the whole tile's compute.
+  auto step = [&](const int t, lchar *const cur_set, lchar *const next_set) {
+    const bool more = t + 1 < wg_hi;
+    if (more) stage.load(rs_k, rs_v, (t + 1) * kBN, tid);
+    if (t >= w_lo && t < w_hi) compute(t, cur_set);
+    if (more) stage.store(next_set, tid);
+    __syncthreads();
+  };
+
+  for (int t = wg_lo; t < wg_hi; t += 2) {
+    step(t, set0, set1);
+    if (t + 1 < wg_hi) step(t + 1, set1, set0);
+  }
+
+  // ---- epilogue: O = O / l (bf16, RNE), lse = ln(sum) + max
+  const float ltot = wave_sum_pair(lsum);
+  const int row = qw0 + l32;
+  if (row < N) {
+    const float inv = 1.0f / ltot;
+    uint16_t *op = prm.o + q_slice + (size_t)row * D + 4 * hh;
+#pragma unroll
+    for (int db = 0; db < g::kDB; ++db) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bf16x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = (__bf16)(oacc[db][4 * i + j] * inv);
+        *(bf16x4 *)(op + 32 * db + 8 * i) = w;
+      }
+    }
+    if (hh == 0) {
+      prm.lse[(size_t)(b * prm.Hq + head) * N + row] = (m2 + __builtin_amdgcn_logf(ltot)) * kLn2;
+    }
+  }
+}
+
+template <int D, int NW, int P>
+hipError_t launch_t(const FwdProblem &p, hipStream_t stream) {
+  constexpr int kRows = 32 * NW / P;
+  Params prm;
+  prm.q = static_cast<const uint16_t *>(p.q);
+  prm.k = static_cast<const uint16_t *>(p.k);
+  prm.v = static_cast<const uint16_t *>(p.v);
+  prm.o = static_cast<uint16_t *>(p.o);
+  prm.lse = p.lse;
+  prm.B = p.B; prm.Hq = p.Hq; prm.Hkv = p.Hkv; prm.N = p.N;
+  prm.G = p.Hq / p.Hkv;
+  prm.groups = p.Hq / P;
+  prm.nq = (p.N + kRows - 1) / kRows;
+  const long long total = (long long)p.B * prm.groups * prm.nq;
+  if (total > 0x7fffffffLL) return hipErrorInvalidValue;
+  prm.total = (int)total;
+  prm.nkt = (p.N + kBN - 1) / kBN;
+  const float c = std::fabs(p.scale) * kLog2e;
+  prm.c = c < FLT_MIN ? FLT_MIN : c;
+  prm.neg = p.scale < 0.0f ? 1 : 0;
+  prm.causal = p.causal;
+  prm.window = p.window;
+  void *args[] = {&prm};
+  return hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_kernel<D, NW, P>),
+                         dim3(prm.total), dim3(NW * 64), args, 0, stream);
+}
+
+template <int D, int NW>
+hipError_t launch_nw(const FwdProblem &p, hipStream_t stream) {
+  const int G = p.Hq / p.Hkv;
+  // heads packed per workgroup: the largest power of two <= NW dividing G
+  if (NW >= 8 && G % 8 == 0) return launch_t<D, NW, (NW >= 8 ? 8 : 1)>(p, stream);
+  if (G % 4 == 0) return launch_t<D, NW, 4>(p, stream);
+  if (G % 2 == 0) return launch_t<D, NW, 2>(p, stream);
+  return launch_t<D, NW, 1>(p, stream);
+}
+
+}  // namespace
+
+const char *variant_name(int variant) {
+  switch (variant) {
+    case kAuto: return "auto";
+    case kWaves4: return "w4_bn64_mfma32x32x16";
+    case kWaves8: return "w8_bn64_mfma32x32x16";
+  }
+  return "invalid";
+}
+
+hipError_t launch_fwd(const FwdProblem &p, int variant, hipStream_t stream) {
+  const int v = variant == kAuto ? kWaves8 : variant;
+  if (p.d == 128) {
+    return v == kWaves4 ? launch_nw<128, 4>(p, stream) : launch_nw<128, 8>(p, stream);
+  }
+  return v == kWaves4 ? launch_nw<64, 4>(p, stream) : launch_nw<64, 8>(p, stream);
+}
+
+}  // namespace attn

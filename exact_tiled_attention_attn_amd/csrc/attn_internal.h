@@ -1,0 +1,33 @@
+// Private interface between the C ABI entry points (attn_api.cpp) and the
+// gfx950 kernels (attn_fwd.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+namespace attn {
+
+// One forward problem, already validated by the entry point.
+struct FwdProblem {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  int B, Hq, Hkv, N, d;
+  float scale;
+  int causal, window;  // window <= 0: none
+};
+
+// Kernel variants selectable through attn_fwd_ex.  Id 0 means "choose".
+enum Variant : int {
+  kAuto = 0,
+  kWaves4 = 1,  // 4 waves (256 threads) per workgroup, 32 query rows per wave
+  kWaves8 = 2,  // 8 waves (512 threads) per workgroup, 32 query rows per wave
+  kNumVariants = 3
+};
+
+const char *variant_name(int variant);
+
+// Enqueue the forward kernel for `p` on `stream`.  Returns the HIP status of
+// the launch call (hipSuccess when it was enqueued).
+hipError_t launch_fwd(const FwdProblem &p, int variant, hipStream_t stream);
+
+}  // namespace attn

@@ -153,8 +153,8 @@ def attention_rows(q, k, v, scale, causal=False, window=0, rows=None, block=256,
 
     Parameters
     ----------
-    q : (B, Hq, N, d) array, any float dtype (widened to float64 exactly
-        when it holds bf16/fp32 values).
+    q : (B, Hq, N, d) array, any float dtype; each (batch, head) slice is
+        widened to float64 (exact for bf16/fp32 values) when it is used.
     k, v : (B, Hkv, N, d) arrays.
     scale : softmax scale; the float32 value is used, widened.
     causal, window : mask flags (window <= 0 means no window).
@@ -165,7 +165,7 @@ def attention_rows(q, k, v, scale, causal=False, window=0, rows=None, block=256,
     Returns ``(o, lse)`` with shapes (B, Hq, R, d) and (B, Hq, R) in float64,
     R = len(rows).
     """
-    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
     B, Hq, Hkv, N, d = _check(q, k, v, causal, window)
     sigma = float(np.float32(scale))
     if not math.isfinite(sigma):
@@ -182,10 +182,11 @@ def attention_rows(q, k, v, scale, causal=False, window=0, rows=None, block=256,
     def one_slice(bh):
         b, h = divmod(bh, Hq)
         kvh = kv_head_of(h, Hq, Hkv)
+        # widened one slice at a time so long inputs stay float32 in memory
+        qh, kh, vh = _as_f64(q[b, h]), _as_f64(k[b, kvh]), _as_f64(v[b, kvh])
         for r0, r1 in blocks:
             sel = rows[r0:r1]
-            ob, lb = _rows_block(q[b, h], k[b, kvh], v[b, kvh], sel, sigma,
-                                 causal, window, N)
+            ob, lb = _rows_block(qh, kh, vh, sel, sigma, causal, window, N)
             o[b, h, r0:r1] = ob
             lse[b, h, r0:r1] = lb
 

@@ -1,0 +1,125 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before any HIP call (so these
+calls launch nothing and never touch the fake pointers passed in)."""
+
+import os
+import re
+
+import pytest
+
+from exact_tiled_attention_attn_amd import attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+# fake, 16-byte aligned, never dereferenced: every call below fails validation
+P = 0x10000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(attn.LIB_PATH):
+        from exact_tiled_attention_attn_amd.build import build
+        build(verbose=False)
+    return attn.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert _declared_functions() == sorted(attn.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_constants_match_header(lib):
+    text = open(HEADER).read()
+    assert int(re.search(r"#define ATTN_ABI_VERSION (\d+)", text).group(1)) == lib.attn_abi_version()
+    assert "(1 << 22)" in text and attn.ATTN_MAX_N == 1 << 22
+    for name, val in (("ATTN_OK", 0), ("ATTN_ERR_INVALID_ARG", 1), ("ATTN_ERR_UNSUPPORTED", 2),
+                      ("ATTN_ERR_LAUNCH", 3)):
+        assert re.search(rf"{name} = {val}\b", text)
+        assert getattr(attn, name) == val
+
+
+def test_status_strings_and_variants(lib):
+    assert attn.attn_status_string(0) == "ok"
+    assert attn.attn_status_string(1) == "invalid argument"
+    assert attn.attn_status_string(2) == "unsupported problem"
+    assert attn.attn_status_string(3) == "kernel launch failed"
+    assert attn.attn_status_string(99) == "unknown status"
+    n = attn.attn_num_variants()
+    assert n >= 2
+    assert attn.attn_variant_name(0) == "auto"
+    names = [attn.attn_variant_name(i) for i in range(n)]
+    assert len(set(names)) == n and "invalid" not in names
+    assert attn.attn_variant_name(n) == "invalid"
+    assert attn.attn_variant_name(-1) == "invalid"
+
+
+GOOD = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, N=64, d=128, scale=0.1, causal=1,
+            window=0)
+
+
+def call(**kw):
+    a = dict(GOOD)
+    a.update(kw)
+    variant = a.pop("variant", None)
+    if variant is None:
+        return attn.attn_fwd(**a)
+    return attn.attn_fwd_ex(**a, variant=variant)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(k=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(v=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(o=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(lse=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(B=-1), attn.ATTN_ERR_INVALID_ARG),
+    (dict(N=-5), attn.ATTN_ERR_INVALID_ARG),
+    (dict(Hq=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(Hkv=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_INVALID_ARG),     # Hq % Hkv != 0
+    (dict(causal=2), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), attn.ATTN_ERR_INVALID_ARG),
+    (dict(variant=-1), attn.ATTN_ERR_INVALID_ARG),
+    (dict(variant=99), attn.ATTN_ERR_INVALID_ARG),
+    (dict(d=96), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(d=256), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(causal=0, window=16), attn.ATTN_ERR_UNSUPPORTED),  # window needs causal
+    (dict(q=P + 8), attn.ATTN_ERR_UNSUPPORTED),               # misaligned
+    (dict(lse=P + 4), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(N=(1 << 22) + 1), attn.ATTN_ERR_UNSUPPORTED),
+])
+def test_rejects_bad_arguments_without_launching(lib, kw, expect):
+    assert call(**kw) == expect
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=0), dict(B=0, q=0, k=0, v=0, o=0, lse=0),
+                                dict(N=0, q=0, k=0, v=0, o=0, lse=0)])
+def test_empty_problem_is_ok_and_launches_nothing(lib, kw):
+    # nothing is launched, so this is safe without a GPU and with null pointers
+    assert call(**kw) == attn.ATTN_OK
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(attn, "_lib", None)
+    monkeypatch.setattr(attn, "LIB_PATH", str(tmp_path / "libattn.so"))
+    with pytest.raises(attn.AttnError):
+        attn.load_library()
+
+
+def test_fwd_wrapper_rejects_host_tensors(lib):
+    import torch
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(attn.AttnError):
+        attn.fwd(q, q, q)
