@@ -62,8 +62,15 @@ def time_workload(w, steps, warmup, variant, torch, attn):
         if st != 0:
             raise RuntimeError(f"attn_fwd_ex: {attn.attn_status_string(st)}")
 
-    for _ in range(warmup):
+    # at least `warmup` launches and at least 0.5 s of them: the clock ramps
+    # up over the first milliseconds of sustained MFMA load
+    t_end = time.perf_counter() + 0.5
+    n = 0
+    while n < warmup or time.perf_counter() < t_end:
         launch()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -80,50 +87,56 @@ def time_workload(w, steps, warmup, variant, torch, attn):
 
 
 def cpu_baseline(w, host, seconds):
-    """The float64 oracle on a bounded sample of the same workload, on the
-    host cores: whole (batch, head) slices' worth of seeded random rows."""
+    """The float64 oracle on the host cores, on the same workload: the whole
+    workload when it fits in about 2 * `seconds`, else a seeded sample of
+    rows over as many (batch, head) slices as fit."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     from exact_tiled_attention_attn_amd.inputs import sample_rows
+    from exact_tiled_attention_attn_amd.workloads import visible_scores_per_head
     from oracle import attention_rows
 
     q, k, v = (t.float().numpy() for t in host)
     cores = len(os.sched_getaffinity(0))
-    rows = sample_rows(w.N, 1024, seed=w.seed * 7919, edges=())
+    G = w.Hq // w.Hkv
 
     def visible(i):
         hi = i + 1 if w.causal else w.N
         lo = max(0, i - w.window + 1) if w.window > 0 else 0
         return hi - lo
 
-    per_slice_scores = sum(visible(int(i)) for i in rows)
-    G = w.Hq // w.Hkv
     with threadpool_limits(limits=1, user_api="blas"):
-        # calibrate on one slice, then size the sample to about `seconds`
+        probe = sample_rows(w.N, 256, seed=w.seed * 7919, edges=())
         t0 = time.perf_counter()
         attention_rows(q[:1, :1], k[:1, :1], v[:1, :1], w.sm_scale, w.causal, w.window,
-                       rows=rows)
-        one = time.perf_counter() - t0
-        nslices = int(max(1, min(w.B * w.Hq, round(seconds * cores / max(one, 1e-3)))))
-        nslices = max(min(nslices, w.B * w.Hq), 1)
+                       rows=probe)
+        rate = sum(visible(int(i)) for i in probe) / (time.perf_counter() - t0)  # scores/s/core
+        full_scores = w.B * w.Hq * visible_scores_per_head(w.N, w.causal, w.window)
+        if full_scores / (rate * cores) <= 2 * seconds:
+            rows, nslices, what = None, w.B * w.Hq, "the whole workload (every row of every head)"
+            scores = full_scores
+        else:
+            rows = sample_rows(w.N, 2048, seed=w.seed * 7919, edges=())
+            per_slice = sum(visible(int(i)) for i in rows)
+            nslices = int(max(1, min(w.B * w.Hq, seconds * rate * cores / per_slice)))
+            scores = per_slice * nslices
+            what = (f"{nslices} (batch, head) slices x {len(rows)} seeded random query rows")
         heads = list(range(nslices))
         qs = np.stack([q[h // w.Hq, h % w.Hq] for h in heads])[None]
         ks = np.stack([k[h // w.Hq, (h % w.Hq) // G] for h in heads])[None]
         vs = np.stack([v[h // w.Hq, (h % w.Hq) // G] for h in heads])[None]
         t0 = time.perf_counter()
-        attention_rows(qs, ks, vs, w.sm_scale, w.causal, w.window, rows=rows,
-                       workers=cores)
+        attention_rows(qs, ks, vs, w.sm_scale, w.causal, w.window, rows=rows, workers=cores)
         dt = time.perf_counter() - t0
-    flops = 4 * w.d * per_slice_scores * nslices
+    flops = 4 * w.d * scores
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": (f"{w.name}: {nslices} (batch, head) slices x {len(rows)} seeded random "
-                   f"query rows each ({per_slice_scores * nslices} unmasked scores), float64 "
-                   f"NumPy, one BLAS thread per worker, {cores} workers, {dt:.1f} s"),
+        "sample": (f"{w.name}: {what} ({scores} unmasked scores), float64 NumPy, one BLAS "
+                   f"thread per worker, {cores} worker threads, {dt:.1f} s"),
         "seconds": dt,
         "cpu": _cpu_model(),
     }

@@ -258,17 +258,60 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
     const lchar *kb = set;
     const lchar *vb = set + g::kTileB;
 
-    // ---- S^T = K Q^T for 64 keys x 32 queries
+    // LDS fragment readers.  K fragment (kk, rb): key row 32*rb + l32, d
+    // chunk 2*kk + hh.  V^T fragment i of the PV sequence (db = i / 4,
+    // rb = (i / 2) % 2, tt = i % 2): two transposed reads of 4 keys each.
+    auto kfrag = [&](int kk, int rb) -> bf16x8 {
+      const int choff = ((2 * kk + hh) ^ k_swz) * 16;
+      return *(const lds_bf16x8_t *)(kb + rb * 32 * g::kRowB + k_row_off + choff);
+    };
+    auto vfrag = [&](int i) -> bf16x8 {
+      const int db = i >> 2, rb = (i >> 1) & 1, tt = i & 1;
+      i16x4 half[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int row = 32 * rb + 16 * tt + 8 * u + v_koff;
+        const int chunk = (4 * db + 2 * v_dgrp + (v_c >> 1)) ^ swz<D>(row);
+        const int off = row * g::kRowB + chunk * 16 + 8 * (v_c & 1);
+        half[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vb + off));
+      }
+      typedef short i16x8 __attribute__((ext_vector_type(8)));
+      const i16x8 both = {half[0][0], half[0][1], half[0][2], half[0][3],
+                          half[1][0], half[1][1], half[1][2], half[1][3]};
+      return __builtin_bit_cast(bf16x8, both);
+    };
+    constexpr int kPV = 4 * g::kDB;  // PV MFMAs per tile
+    constexpr int kKA = 3;           // K ring depth (k-steps in flight)
+    constexpr int kVA = 4;           // V ring depth (MFMAs in flight)
+
+    // ---- S^T = K Q^T for 64 keys x 32 queries; K reads run kKA-1 k-steps
+    // ahead of the MFMAs that consume them (sched_barrier fences keep the
+    // compiler from sinking each read onto its MFMA, which would expose the
+    // full LDS latency on every MFMA).
     f32x16 s[2] = {f32x16{}, f32x16{}};
+    bf16x8 ka[kKA][2];
+#pragma unroll
+    for (int kk = 0; kk < kKA - 1; ++kk) {
+      ka[kk][0] = kfrag(kk, 0);
+      ka[kk][1] = kfrag(kk, 1);
+    }
 #pragma unroll
     for (int kk = 0; kk < g::kKSteps; ++kk) {
-      const int choff = (((2 * kk + hh) ^ k_swz)) * 16;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const bf16x8 a = *(const lds_bf16x8_t *)(kb + rb * 32 * g::kRowB + k_row_off + choff);
-        s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[rb], 0, 0, 0);
+      if (kk + kKA - 1 < g::kKSteps) {
+        ka[(kk + kKA - 1) % kKA][0] = kfrag(kk + kKA - 1, 0);
+        ka[(kk + kKA - 1) % kKA][1] = kfrag(kk + kKA - 1, 1);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % kKA][0], qf[kk], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % kKA][1], qf[kk], s[1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // the first V^T fragments do not depend on P: start them now so the
+    // softmax hides their latency
+    bf16x8 va[kVA];
+#pragma unroll
+    for (int i = 0; i < kVA; ++i) va[i] = vfrag(i);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- mask: only tiles that hold a masked (row, key) pair for this wave
     const bool need_mask = (prm.causal && j0 + kBN - 1 > qw0) ||
@@ -321,28 +364,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
       }
     }
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T; V reads run kVA MFMAs ahead
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int db = 0; db < g::kDB; ++db) {
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          i16x4 half[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int row = 32 * rb + 16 * tt + 8 * u + v_koff;
-            const int chunk = (4 * db + 2 * v_dgrp + (v_c >> 1)) ^ swz<D>(row);
-            const int off = row * g::kRowB + chunk * 16 + 8 * (v_c & 1);
-            half[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vb + off));
-          }
-          typedef short i16x8 __attribute__((ext_vector_type(8)));
-          i16x8 both = {half[0][0], half[0][1], half[0][2], half[0][3],
-                        half[1][0], half[1][1], half[1][2], half[1][3]};
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both),
-                                                             pf[rb][tt], oacc[db], 0, 0, 0);
-        }
-      }
+    for (int i = 0; i < kPV; ++i) {
+      const int db = i >> 2, rb = (i >> 1) & 1, tt = i & 1;
+      const bf16x8 a = va[i % kVA];
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[rb][tt], oacc[db], 0, 0, 0);
+      if (i + kVA < kPV) va[i % kVA] = vfrag(i + kVA);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
