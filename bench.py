@@ -36,8 +36,16 @@ def log(msg):
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of the kernel source with // comments, trailing blanks and
+    empty lines removed: a comment edit keeps stored counter data valid, any
+    code change invalidates it."""
+    code = []
+    with open(KERNEL_SRC) as f:
+        for line in f:
+            line = line.split("//", 1)[0].rstrip()
+            if line:
+                code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def device_inputs(w, torch):
@@ -126,9 +134,19 @@ def cpu_baseline(w, host, seconds):
         qs = np.stack([q[h // w.Hq, h % w.Hq] for h in heads])[None]
         ks = np.stack([k[h // w.Hq, (h % w.Hq) // G] for h in heads])[None]
         vs = np.stack([v[h // w.Hq, (h % w.Hq) // G] for h in heads])[None]
+        # repeat the sample until about `seconds` of CPU time have passed, so
+        # a workload that the host finishes quickly is still timed stably
+        reps = 0
         t0 = time.perf_counter()
-        attention_rows(qs, ks, vs, w.sm_scale, w.causal, w.window, rows=rows, workers=cores)
-        dt = time.perf_counter() - t0
+        while True:
+            attention_rows(qs, ks, vs, w.sm_scale, w.causal, w.window, rows=rows, workers=cores)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= seconds or dt * (reps + 1) / reps > 2 * seconds:
+                break
+    if reps > 1:
+        what += f", {reps} passes"
+    scores *= reps
     flops = 4 * w.d * scores
     return {
         "value": flops / dt / 1e12,

@@ -27,11 +27,15 @@
 //   ds_read_b64_tr_b16: in each 16-lane group, lane 4j+c supplies the address
 //   of 4 consecutive d values of key row j and lane i receives the 4 keys of
 //   column i.
-// * K and V tiles go HBM -> LDS with buffer_load ... lds (16 bytes per lane,
-//   no VGPR staging), double-buffered.  The buffer descriptor spans one
-//   (batch, KV-head) slice, so keys past N read as zero.  Inside a row the
-//   16-byte chunks are XOR-swizzled so that both the b128 K reads and the
-//   transposed V reads hit distinct LDS banks.
+// * K and V tiles go HBM -> registers -> LDS, 16 bytes per lane per load,
+//   double-buffered: the loads of tile t+1 are issued before tile t is
+//   computed and written to the other LDS buffer after it, so their latency
+//   hides behind a whole tile of MFMAs.  (Direct buffer_load ... lds would
+//   save the registers, but the compiler then waits for every outstanding
+//   vector load before each transposed LDS read.)  The buffer descriptor
+//   spans one (batch, KV-head) slice, so keys past N read as zero.  Inside a
+//   row the 16-byte chunks are XOR-swizzled so that both the b128 K reads
+//   and the transposed V reads hit distinct LDS banks.
 // * GQA: the query heads sharing a KV head are packed into one workgroup
 //   (one head per wave), so each K/V tile is loaded once for all of them.
 // * The running max is exact.  When no row of the wave gets a larger max
