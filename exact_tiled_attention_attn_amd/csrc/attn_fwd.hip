@@ -57,6 +57,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((vector_size(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -64,6 +65,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
 
 constexpr int kBN = 64;              // keys per tile
+constexpr float kTau = 8.0f;         // lazy-rescale threshold, log2 units
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kBufferFlags = 0x00020000;  // gfx9 buffer descriptor word 3
@@ -86,21 +88,20 @@ struct Params {
 
 template <int D>
 struct Geo {
-  static constexpr int kRowB = D * 2;           // bytes per K/V row
+  static constexpr int kRowB = D * 2;           // bytes per K/V row in HBM
   static constexpr int kCh = kRowB / 16;        // 16-byte chunks per row
-  static constexpr int kTileB = kBN * kRowB;    // bytes per K or V tile
+  // LDS row strides.  K rows are padded by 16 bytes, so the 16 rows one
+  // ds_read_b128 phase touches start 4 banks apart; V rows by 64 bytes, so
+  // the 4 consecutive rows of a transposed read start 16 banks apart.  Every
+  // fragment address is then a per-lane base plus a compile-time offset.
+  static constexpr int kKStride = kRowB + 16;
+  static constexpr int kVStride = kRowB + 64;
+  static constexpr int kKTileB = kBN * kKStride;
+  static constexpr int kVTileB = kBN * kVStride;
+  static constexpr int kSetB = kKTileB + kVTileB;  // one K tile + one V tile
   static constexpr int kKSteps = D / 16;        // MFMA k-steps of S^T
   static constexpr int kDB = D / 32;            // 32-wide d blocks of O^T
 };
-
-// Chunk swizzle of LDS row r (see the header comment).  For D = 128, the 16
-// rows read together by a b128 phase get distinct chunk masks, and the 4
-// consecutive rows of a transposed V read get masks differing in bits 2..3.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return (r >> 1) & 7;
-}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufferFlags);
@@ -139,16 +140,17 @@ struct TileStage {
       v[n] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0);
     }
   }
-  // Write into an LDS buffer set (K tile, then V tile), chunk p of row r at
-  // position p ^ swz(r).
+  // Write into an LDS buffer set: the K tile at offset 0, the V tile at
+  // kKTileB, each row at its padded stride.
   __device__ __forceinline__ void store(lchar *set, int tid) const {
+    const int r0 = tid / g::kCh, p = tid % g::kCh;
+    lchar *kp = set + r0 * g::kKStride + p * 16;
+    lchar *vp = set + g::kKTileB + r0 * g::kVStride + p * 16;
+    constexpr int kRowsPerLoad = NW * 64 / g::kCh;
 #pragma unroll
     for (int n = 0; n < kLoads; ++n) {
-      const int ci = n * NW * 64 + tid;
-      const int r = ci / g::kCh, p = ci % g::kCh;
-      const int off = r * g::kRowB + ((p ^ swz<D>(r)) * 16);
-      *(__attribute__((address_space(3))) u32x4 *)(set + off) = k[n];
-      *(__attribute__((address_space(3))) u32x4 *)(set + g::kTileB + off) = v[n];
+      *(__attribute__((address_space(3))) u32x4 *)(kp + n * kRowsPerLoad * g::kKStride) = k[n];
+      *(__attribute__((address_space(3))) u32x4 *)(vp + n * kRowsPerLoad * g::kVStride) = v[n];
     }
   }
 };
@@ -169,9 +171,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
   constexpr int kRows = 32 * NW / P;  // query rows per workgroup
 
   // Two LDS buffer sets, each a K tile followed by a V tile.
-  __shared__ __attribute__((aligned(1024))) char smem[4 * g::kTileB];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * g::kSetB];
   lchar *const set0 = (lchar *)smem;
-  lchar *const set1 = (lchar *)smem + 2 * g::kTileB;
+  lchar *const set1 = (lchar *)smem + g::kSetB;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -231,21 +233,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
   }
 
   // per-lane LDS byte offsets
-  // K (b128): row 32*rb + l32, chunk (2*kk + hh) ^ swz(l32)
-  const int k_row_off = l32 * g::kRowB;
-  const int k_swz = swz<D>(l32);
-  // V (tr read): key row 32rb + 16t + 8u + koff, d = 32db + doff
-  const int v_koff = 4 * hh + ((lane & 15) >> 2);
-  const int v_dgrp = (lane >> 4) & 1;      // which 16-wide half of the 32-d block
-  const int v_c = lane & 3;                // which 4-wide piece of the 16
-  // chunk index (before swizzle) of d = 32db + 16*v_dgrp + 4*v_c is
-  // 4*db + 2*v_dgrp + (v_c >> 1); byte within the chunk 8*(v_c & 1).
+  // K (b128): key row 32*rb + l32, d = 16*kk + 8*hh .. +7
+  const int k_lane = l32 * g::kKStride + hh * 16;
+  // V (transposed read): key row 32rb + 16tt + 8u + 4hh + (lane & 15) / 4,
+  // d = 32db + 16*((lane >> 4) & 1) + 4*(lane & 3) .. +3
+  const int v_lane = (4 * hh + ((lane & 15) >> 2)) * g::kVStride +
+                     (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
   f32x16 oacc[g::kDB];
 #pragma unroll
   for (int i = 0; i < g::kDB; ++i) oacc[i] = f32x16{};
   float m2 = -1e30f;   // running max, scaled log2 units (finite: no inf - inf)
   float lsum = 0.0f;   // this lane's partial row sum (its 32 of every 64 keys)
+  float lrnd = 0.0f;   // the same over the bf16-rounded weights
   const float c = prm.c;
 
   TileStage<D, NW> stage;
@@ -259,24 +259,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
   auto compute = [&](const int t, const lchar *const set) {
 
     const int j0 = t * kBN;
-    const lchar *kb = set;
-    const lchar *vb = set + g::kTileB;
+    const lchar *kb = set + k_lane;
+    const lchar *vb = set + g::kKTileB + v_lane;
 
     // LDS fragment readers.  K fragment (kk, rb): key row 32*rb + l32, d
     // chunk 2*kk + hh.  V^T fragment i of the PV sequence (db = i / 4,
     // rb = (i / 2) % 2, tt = i % 2): two transposed reads of 4 keys each.
     auto kfrag = [&](int kk, int rb) -> bf16x8 {
-      const int choff = ((2 * kk + hh) ^ k_swz) * 16;
-      return *(const lds_bf16x8_t *)(kb + rb * 32 * g::kRowB + k_row_off + choff);
+      return *(const lds_bf16x8_t *)(kb + rb * 32 * g::kKStride + kk * 32);
     };
     auto vfrag = [&](int i) -> bf16x8 {
       const int db = i >> 2, rb = (i >> 1) & 1, tt = i & 1;
       i16x4 half[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int row = 32 * rb + 16 * tt + 8 * u + v_koff;
-        const int chunk = (4 * db + 2 * v_dgrp + (v_c >> 1)) ^ swz<D>(row);
-        const int off = row * g::kRowB + chunk * 16 + 8 * (v_c & 1);
+        const int off = (32 * rb + 16 * tt + 8 * u) * g::kVStride + db * 64;
         half[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vb + off));
       }
       typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -321,16 +318,23 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
     const bool need_mask = (prm.causal && j0 + kBN - 1 > qw0) ||
                            (prm.window > 0 && j0 <= qw0 + 31 - prm.window) || (j0 + kBN > N);
     if (need_mask) {
+      // Register r of block rb holds key kbase + off with the compile-time
+      // off = 32*rb + 8*(r/4) + r%4.  The keys this lane's row sees form the
+      // range lo < off <= hi relative to kbase, so one unsigned compare per
+      // register decides visibility: (unsigned)(off - lo - 1) < hi - lo.
       const int qrow = qw0 + l32;
       const int kbase = j0 + 4 * hh;
+      int hi = N - 1 - kbase;
+      if (prm.causal) hi = min(hi, qrow - kbase);
+      const int lo = prm.window > 0 ? qrow - prm.window - kbase : -1 - kbase;
+      const unsigned span = (unsigned)max(hi - lo, 0);
+      const int lo1 = lo + 1;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kbase + 32 * rb + 8 * (r >> 2) + (r & 3);
-          bool vis = key < N;
-          if (prm.causal) vis = vis && key <= qrow;
-          if (prm.window > 0) vis = vis && key > qrow - prm.window;
+          const int off = 32 * rb + 8 * (r >> 2) + (r & 3);
+          const bool vis = (unsigned)(off - lo1) < span;
           s[rb][r] = vis ? s[rb][r] : -INFINITY;
         }
       }
@@ -344,17 +348,23 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
     mx = wave_max_pair(mx);
     const float mt2 = mx * c;
-    const bool grow = mt2 > m2;
+    // Lazy rescale: the reference point m2 only moves (and O is rescaled)
+    // when some row's tile max exceeds it by more than kTau (log2 units), so
+    // P <= 2^kTau; most tiles skip the 64 multiplies.  When it moves, every
+    // row of the wave takes its exact running max.
+    const bool grow = mt2 > m2 + kTau;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float mnew = fmaxf(m2, mt2);
       const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
       lsum *= alpha;
+      lrnd *= alpha;
 #pragma unroll
       for (int i = 0; i < g::kDB; ++i) oacc[i] *= alpha;
       m2 = mnew;
     }
     const float negm = -m2;
     bf16x8 pf[2][2];
+    float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent add chains
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
@@ -362,10 +372,31 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][8 * tt + e], c, negm));
-          lsum += p;
+          part[e & 3] += p;
           pf[rb][tt][e] = (__bf16)p;
         }
       }
+    }
+    lsum += (part[0] + part[1]) + (part[2] + part[3]);
+    // The same weights as the PV MFMA sees them (bf16), summed with
+    // v_dot2_f32_bf16 against (1, 1): normalizing O by this sum makes a row
+    // dominated by one key return that key's V row up to fp32 rounding, even
+    // when its weight is not exactly 1.0 (lazy rescale).
+    {
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      float rp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2 pair = {pf[rb][tt][2 * e], pf[rb][tt][2 * e + 1]};
+            rp[e] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, rp[e], false);
+          }
+        }
+      }
+      lrnd += (rp[0] + rp[1]) + (rp[2] + rp[3]);
     }
 
     // ---- O^T += V^T P^T; V reads run kVA MFMAs ahead
@@ -399,9 +430,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
 
   // ---- epilogue: O = O / l (bf16, RNE), lse = ln(sum) + max
   const float ltot = wave_sum_pair(lsum);
+  const float lrtot = wave_sum_pair(lrnd);
   const int row = qw0 + l32;
   if (row < N) {
-    const float inv = 1.0f / ltot;
+    const float inv = 1.0f / lrtot;
     uint16_t *op = prm.o + q_slice + (size_t)row * D + 4 * hh;
 #pragma unroll
     for (int db = 0; db < g::kDB; ++db) {

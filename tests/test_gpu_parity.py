@@ -287,3 +287,21 @@ def test_workload_parity(name):
         lrf.append(l_r)
     check(torch.cat(og), torch.cat(lg), np.concatenate(orf), np.concatenate(lrf),
           f"{name} ({len(rows_of(0))} rows/head)")
+
+
+@pytest.mark.parametrize("name", ["c2_causal_mha", "c2_causal_mha_sharp", "c3_causal_window",
+                                  "c4_causal_gqa"])
+def test_workload_parity_every_row(name):
+    """The full-size launch checked on every row of every head: the oracle
+    covers these workloads in seconds on the host cores, so the worst row
+    (not only a sample) must meet the bar."""
+    w = WORKLOADS[name]
+    say(f"case workload {name} (every row)")
+    q, k, v = _inputs(w)
+    o, lse = run(q, k, v, w.causal, w.window, scale=w.sm_scale)
+    from threadpoolctl import threadpool_limits
+    qf, kf, vf = q.float().numpy(), k.float().numpy(), v.float().numpy()
+    with threadpool_limits(limits=1, user_api="blas"):
+        o_ref, l_ref = attention_forward(qf, kf, vf, w.sm_scale, w.causal, w.window,
+                                         workers=16)
+    check(o, lse, o_ref, l_ref, f"{name} (every row)")
