@@ -22,9 +22,12 @@ LIB_PATH = os.path.join(HERE, "libattn.so")
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall"]
-# Packed fp32 VALU forms are kept out of the device code.
+# Packed fp32 VALU forms are kept out of the device code.  -fno-honor-nans:
+# no value in the kernels is NaN unless an input is, and without it every
+# fmax of an MFMA result first quiets a possible signaling NaN (one extra
+# instruction per score).  Infinities (the -inf of masked scores) are kept.
 DEVICE_ONLY = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-               "-packed-fp32-ops"]
+               "-packed-fp32-ops", "-fno-honor-nans"]
 
 
 def _hipcc() -> str:

@@ -8,8 +8,8 @@
 // How: the score matrix is produced one 64-key tile at a time on chip and
 // folded into a running output with the running (max, sum) softmax of the
 // same page's section "FlashAttention: exact attention, IO-aware"; tiles that
-// no row of a wave can see are never visited ("Against the real libraries":
-// mask structure becomes loop bounds).
+// no row can see are never visited ("Against the real libraries": mask
+// structure becomes loop bounds).
 //
 // Mapping onto CDNA4
 // ------------------
@@ -27,22 +27,23 @@
 //   ds_read_b64_tr_b16: in each 16-lane group, lane 4j+c supplies the address
 //   of 4 consecutive d values of key row j and lane i receives the 4 keys of
 //   column i.
-// * K and V tiles go HBM -> registers -> LDS, 16 bytes per lane per load,
-//   double-buffered: the loads of tile t+1 are issued before tile t is
-//   computed and written to the other LDS buffer after it, so their latency
-//   hides behind a whole tile of MFMAs.  (Direct buffer_load ... lds would
-//   save the registers, but the compiler then waits for every outstanding
-//   vector load before each transposed LDS read.)  The buffer descriptor
-//   spans one (batch, KV-head) slice, so keys past N read as zero.  Inside a
-//   row the 16-byte chunks are XOR-swizzled so that both the b128 K reads
-//   and the transposed V reads hit distinct LDS banks.
+// * K and V tiles go HBM -> registers -> LDS, 16 bytes per lane per load.
+//   The loads of a later tile are issued a whole tile of MFMAs before their
+//   LDS stores.  (Direct buffer_load ... lds would save the registers, but
+//   the compiler then waits for every outstanding vector load before each
+//   transposed LDS read.)  The buffer descriptor spans one (batch, KV-head)
+//   slice, so keys past N read as zero.  LDS rows are padded so both the
+//   b128 K reads and the transposed V reads hit distinct banks.
 // * GQA: the query heads sharing a KV head are packed into one workgroup
 //   (one head per wave), so each K/V tile is loaded once for all of them.
-// * The running max is exact.  When no row of the wave gets a larger max
-//   from a tile (the common case once a row has seen a few tiles), the
-//   rescale of the O accumulator is skipped with one wave-uniform branch.
-//   An exact max keeps the largest weight of every row at exactly 1.0, so
-//   the bf16 rounding of P never touches the dominant term of a sharp row.
+// * Online softmax with a lazy reference max: O is rescaled only when a
+//   row's tile max exceeds the reference by more than 2^kTau, and O is
+//   normalized by the sum of the bf16 weights the MFMA actually used.
+//
+// Schedule: per key tile, every wave runs S, softmax and PV between two
+// workgroup barriers; the two waves that share a SIMD (8-wave variant) run
+// their softmax together, which is what keeps the vector ALU busy: one wave
+// alone issues a vector instruction only every few clocks.
 
 #include <hip/hip_runtime.h>
 
@@ -60,9 +61,11 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((vector_size(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void_t;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
+typedef char __attribute__((address_space(3))) lchar;
 
 constexpr int kBN = 64;              // keys per tile
 constexpr float kTau = 8.0f;         // lazy-rescale threshold, log2 units
@@ -101,6 +104,8 @@ struct Geo {
   static constexpr int kSetB = kKTileB + kVTileB;  // one K tile + one V tile
   static constexpr int kKSteps = D / 16;        // MFMA k-steps of S^T
   static constexpr int kDB = D / 32;            // 32-wide d blocks of O^T
+  static constexpr int kS = 2 * kKSteps;        // S MFMAs per tile
+  static constexpr int kPV = 4 * kDB;           // PV MFMAs per tile
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -116,13 +121,11 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
   return x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
 }
 
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef char __attribute__((address_space(3))) lchar;
-
-// This thread's share of one K or V tile: kLoads 16-byte chunks.  Chunk
-// n covers tile row r = ci / kCh, chunk p = ci % kCh with
-// ci = n * NW * 64 + tid, so each wave instruction reads whole rows
-// contiguously from HBM.  Keys past N read as zero (buffer range check).
+// This thread's share of one K tile and one V tile (possibly of different
+// key tiles): kLoads 16-byte chunks each.  Chunk n covers tile row
+// r = ci / kCh, chunk p = ci % kCh with ci = n * NW * 64 + tid, so each wave
+// instruction reads whole rows contiguously from HBM.  Keys past N read as
+// zero (buffer range check).
 template <int D, int NW>
 struct TileStage {
   using g = Geo<D>;
@@ -130,27 +133,26 @@ struct TileStage {
   static_assert(kLoads * NW * 64 == kBN * g::kCh, "tile must split evenly over the threads");
   u32x4 k[kLoads], v[kLoads];
 
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int j0,
-                                       int tid) {
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                       int jk0, int jv0, int tid) {
 #pragma unroll
     for (int n = 0; n < kLoads; ++n) {
       const int ci = n * NW * 64 + tid;
-      const int voff = j0 * g::kRowB + ci * 16;
-      k[n] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff, 0, 0);
-      v[n] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0);
+      k[n] = __builtin_amdgcn_raw_buffer_load_b128(rk, jk0 * g::kRowB + ci * 16, 0, 0);
+      v[n] = __builtin_amdgcn_raw_buffer_load_b128(rv, jv0 * g::kRowB + ci * 16, 0, 0);
     }
   }
-  // Write into an LDS buffer set: the K tile at offset 0, the V tile at
-  // kKTileB, each row at its padded stride.
-  __device__ __forceinline__ void store(lchar *set, int tid) const {
+  // Write the K chunks into the K tile at `kt` and the V chunks into the V
+  // tile at `vt`, each row at its padded stride.
+  __device__ __forceinline__ void store(lchar *kt, lchar *vt, int tid) const {
     const int r0 = tid / g::kCh, p = tid % g::kCh;
-    lchar *kp = set + r0 * g::kKStride + p * 16;
-    lchar *vp = set + g::kKTileB + r0 * g::kVStride + p * 16;
+    lchar *kp = kt + r0 * g::kKStride + p * 16;
+    lchar *vp = vt + r0 * g::kVStride + p * 16;
     constexpr int kRowsPerLoad = NW * 64 / g::kCh;
 #pragma unroll
     for (int n = 0; n < kLoads; ++n) {
-      *(__attribute__((address_space(3))) u32x4 *)(kp + n * kRowsPerLoad * g::kKStride) = k[n];
-      *(__attribute__((address_space(3))) u32x4 *)(vp + n * kRowsPerLoad * g::kVStride) = v[n];
+      *(lds_u32x4_t *)(kp + n * kRowsPerLoad * g::kKStride) = k[n];
+      *(lds_u32x4_t *)(vp + n * kRowsPerLoad * g::kVStride) = v[n];
     }
   }
 };
@@ -165,6 +167,239 @@ __device__ __forceinline__ float wave_sum_pair(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
+// Which (batch, head, rows, key tiles) a wave of a workgroup owns.
+struct Task {
+  int b, head, kvh;
+  int qw0;             // first query row of this wave
+  int wg_lo, wg_hi;    // key tiles any row of the workgroup sees
+  int w_lo, w_hi;      // key tiles any row of this wave sees
+  size_t q_slice;      // (b * Hq + head) * N: first row of the Q / O slice
+  size_t kv_slice;     // (b * Hkv + kvh) * N: first row of the K / V slice
+};
+
+// kRows query rows per workgroup, P heads per workgroup (wave w serves head
+// w % P on rows (w / P) * 32 ..).
+template <int P, int kRows>
+__device__ __forceinline__ Task make_task(const Params &prm, int wave) {
+  Task tk;
+  const int logical = xcd_remap(blockIdx.x, prm.total);
+  const int qrank = logical % prm.nq;
+  const int hgb = logical / prm.nq;
+  const int hg = hgb % prm.groups;
+  tk.b = hgb / prm.groups;
+  const int qi = prm.causal ? (prm.nq - 1 - qrank) : qrank;  // heaviest tiles first
+  tk.head = hg * P + (wave % P);
+  tk.kvh = __builtin_amdgcn_readfirstlane((hg * P) / prm.G);  // P divides G
+  const int wg_r0 = qi * kRows;
+  tk.qw0 = wg_r0 + (wave / P) * 32;
+  const int N = prm.N;
+  auto tile_range = [&](int r0, int r1, int &lo, int &hi) {  // rows [r0, r1)
+    hi = prm.causal ? min(prm.nkt, (r1 - 1) / kBN + 1) : prm.nkt;
+    lo = prm.window > 0 ? max(0, r0 - prm.window + 1) / kBN : 0;
+  };
+  tile_range(wg_r0, min(N, wg_r0 + kRows), tk.wg_lo, tk.wg_hi);
+  if (tk.qw0 < N) {
+    tile_range(tk.qw0, min(N, tk.qw0 + 32), tk.w_lo, tk.w_hi);
+  } else {
+    tk.w_lo = tk.w_hi = 0;  // rows past the end: this wave only helps load tiles
+  }
+  tk.kv_slice = (size_t)(tk.b * prm.Hkv + tk.kvh) * N;
+  tk.q_slice = (size_t)(tk.b * prm.Hq + tk.head) * N;
+  return tk;
+}
+
+// Q^T operand: lane holds query row qw0 + l32, d = 16*kk + 8*hh + s.
+template <int D>
+__device__ __forceinline__ void load_q(const Params &prm, const Task &tk, int l32, int hh,
+                                       bf16x8 (&qf)[Geo<D>::kKSteps]) {
+  const int row = tk.qw0 + l32;
+  const uint16_t *qp = prm.q + tk.q_slice * D + (size_t)row * D + 8 * hh;
+#pragma unroll
+  for (int kk = 0; kk < Geo<D>::kKSteps; ++kk) {
+    qf[kk] = row < prm.N ? *(const bf16x8 *)(qp + 16 * kk) : bf16x8{};
+    if (prm.neg) {
+      u32x4 t = __builtin_bit_cast(u32x4, qf[kk]);
+      t ^= 0x80008000u;
+      qf[kk] = __builtin_bit_cast(bf16x8, t);
+    }
+  }
+}
+
+// Per-lane LDS byte offsets of the MFMA fragments.
+// K (b128): key row 32*rb + l32, d = 16*kk + 8*hh .. +7.
+template <int D>
+__device__ __forceinline__ int k_lane_off(int lane) {
+  return (lane & 31) * Geo<D>::kKStride + (lane >> 5) * 16;
+}
+// V (transposed read): key row 32rb + 16tt + 8u + 4hh + (lane & 15) / 4,
+// d = 32db + 16*((lane >> 4) & 1) + 4*(lane & 3) .. +3.
+template <int D>
+__device__ __forceinline__ int v_lane_off(int lane) {
+  return (4 * (lane >> 5) + ((lane & 15) >> 2)) * Geo<D>::kVStride +
+         (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+}
+// K fragment (k-step kk, key block rb) from a K tile base already offset by
+// k_lane_off.
+template <int D>
+__device__ __forceinline__ bf16x8 kfrag(const lchar *kb, int kk, int rb) {
+  return *(const lds_bf16x8_t *)(kb + rb * 32 * Geo<D>::kKStride + kk * 32);
+}
+// V^T fragment (d block db, key block rb, 16-key half tt) from a V tile base
+// already offset by v_lane_off: two transposed reads of 4 keys each.
+template <int D>
+__device__ __forceinline__ bf16x8 vfrag(const lchar *vb, int db, int rb, int tt) {
+  const lchar *p = vb + (32 * rb + 16 * tt) * Geo<D>::kVStride + db * 64;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(p + 8 * Geo<D>::kVStride));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+// Running softmax state of the lane's query row (its half of the keys).
+struct RowState {
+  float m2 = -1e30f;   // reference max, scaled log2 units (finite: no inf - inf)
+  float lsum = 0.0f;   // sum of the fp32 weights (gives lse)
+  float lrnd = 0.0f;   // sum of the bf16-rounded weights (normalizes O)
+};
+
+// Whether key tile j0 holds a (row, key) pair that a row of the wave's 32
+// rows qw0.. cannot see: the causal diagonal, the window edge and the tile
+// holding key N - 1.  Wave-uniform.
+__device__ __forceinline__ bool tile_needs_mask(const Params &prm, int j0, int qw0) {
+  return (prm.causal && j0 + kBN - 1 > qw0) ||
+         (prm.window > 0 && j0 <= qw0 + 31 - prm.window) || (j0 + kBN > prm.N);
+}
+
+// Scores of keys this lane's row cannot see become -inf (no branches).
+__device__ __forceinline__ void apply_mask(f32x16 (&s)[2], const Params &prm, int j0, int qw0,
+                                           int l32, int hh) {
+  const int N = prm.N;
+  // Register r of block rb holds key kbase + off with the compile-time
+  // off = 32*rb + 8*(r/4) + r%4.  The keys this lane's row sees form the
+  // range lo < off <= hi relative to kbase, so one unsigned compare per
+  // register decides visibility: (unsigned)(off - lo - 1) < hi - lo.
+  const int qrow = qw0 + l32;
+  const int kbase = j0 + 4 * hh;
+  int hi = N - 1 - kbase;
+  if (prm.causal) hi = min(hi, qrow - kbase);
+  const int lo = prm.window > 0 ? qrow - prm.window - kbase : -1 - kbase;
+  const unsigned span = (unsigned)max(hi - lo, 0);
+  const int lo1 = lo + 1;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int off = 32 * rb + 8 * (r >> 2) + (r & 3);
+      const bool vis = (unsigned)(off - lo1) < span;
+      s[rb][r] = vis ? s[rb][r] : -INFINITY;
+    }
+  }
+}
+
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], const Params &prm, int j0, int qw0,
+                                          int l32, int hh) {
+  if (tile_needs_mask(prm, j0, qw0)) apply_mask(s, prm, j0, qw0, l32, hh);
+}
+
+// Online softmax of one tile of scores (scaled log2 domain), without
+// branches: new tile max; lazy move of the reference max m2 (it moves only
+// when some row's tile max exceeds it by more than kTau log2 units, so
+// P <= 2^kTau, and then every row of the wave takes its exact running max);
+// P = exp2(c*S - m2) packed to bf16 as the B operand of the PV MFMAs; both
+// running sums.  Returns whether m2 moved; the caller then multiplies O by
+// `alpha` before the next PV MFMA.
+__device__ __forceinline__ bool softmax_core(const f32x16 (&s)[2], bf16x8 (&pf)[2][2],
+                                             RowState &st, float c, float &alpha) {
+  float mq[4];  // four independent max chains
+#pragma unroll
+  for (int j = 0; j < 4; ++j) mq[j] = fmaxf(s[j >> 1][8 * (j & 1)], s[j >> 1][8 * (j & 1) + 1]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int e = 2; e < 8; ++e) mq[j] = fmaxf(mq[j], s[j >> 1][8 * (j & 1) + e]);
+  }
+  const float mx = wave_max_pair(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
+  const float mt2 = mx * c;
+  const bool move = __builtin_amdgcn_ballot_w64(mt2 > st.m2 + kTau) != 0;
+  const float mnew = move ? fmaxf(st.m2, mt2) : st.m2;
+  alpha = __builtin_amdgcn_exp2f(st.m2 - mnew);
+  st.lsum *= alpha;
+  st.lrnd *= alpha;
+  st.m2 = mnew;
+  const float negm = -st.m2;
+  float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent add chains
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][8 * tt + e], c, negm));
+        part[e & 3] += p;
+        pf[rb][tt][e] = (__bf16)p;
+      }
+    }
+  }
+  st.lsum += (part[0] + part[1]) + (part[2] + part[3]);
+  // The same weights as the PV MFMA sees them (bf16), summed with
+  // v_dot2_f32_bf16 against (1, 1): normalizing O by this sum makes a row
+  // dominated by one key return that key's V row up to fp32 rounding, even
+  // when its weight is not exactly 1.0 (lazy rescale).
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float rp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pair = {pf[rb][tt][2 * e], pf[rb][tt][2 * e + 1]};
+        rp[e] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, rp[e], false);
+      }
+    }
+  }
+  st.lrnd += (rp[0] + rp[1]) + (rp[2] + rp[3]);
+  return move;
+}
+
+template <int KDB>
+__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], bf16x8 (&pf)[2][2],
+                                             RowState &st, f32x16 (&oacc)[KDB], float c) {
+  float alpha;
+  if (softmax_core(s, pf, st, c, alpha)) {
+#pragma unroll
+    for (int i = 0; i < KDB; ++i) oacc[i] *= alpha;
+  }
+}
+
+// Epilogue: O = O / lrnd (bf16, RNE) and lse = ln(lsum) + max.
+template <int D>
+__device__ __forceinline__ void write_out(const Params &prm, const Task &tk, int l32, int hh,
+                                          const f32x16 (&oacc)[Geo<D>::kDB], const RowState &st) {
+  const float ltot = wave_sum_pair(st.lsum);
+  const float lrtot = wave_sum_pair(st.lrnd);
+  const int row = tk.qw0 + l32;
+  if (row >= prm.N) return;
+  const float inv = 1.0f / lrtot;
+  uint16_t *op = prm.o + tk.q_slice * D + (size_t)row * D + 4 * hh;
+#pragma unroll
+  for (int db = 0; db < Geo<D>::kDB; ++db) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = (__bf16)(oacc[db][4 * i + j] * inv);
+      *(bf16x4 *)(op + 32 * db + 8 * i) = w;
+    }
+  }
+  if (hh == 0) prm.lse[tk.q_slice + row] = (st.m2 + __builtin_amdgcn_logf(ltot)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// Lockstep schedule: per key tile, every wave computes S, softmax and PV
+// between two workgroup barriers.
+// ---------------------------------------------------------------------------
 template <int D, int NW, int P>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
   using g = Geo<D>;
@@ -180,110 +415,35 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
 
-  // ---- which (batch, head, rows) this workgroup and wave own
-  const int logical = xcd_remap(blockIdx.x, prm.total);
-  const int qrank = logical % prm.nq;
-  const int hgb = logical / prm.nq;
-  const int hg = hgb % prm.groups, b = hgb / prm.groups;
-  const int qi = prm.causal ? (prm.nq - 1 - qrank) : qrank;  // heaviest tiles first
-  const int head = hg * P + (wave % P);
-  const int kvh = __builtin_amdgcn_readfirstlane((hg * P) / prm.G);
-  const int wg_r0 = qi * kRows;
-  const int qw0 = wg_r0 + (wave / P) * 32;  // first row of this wave
+  const Task tk = make_task<P, kRows>(prm, wave);
   const int N = prm.N;
+  const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(prm.k + tk.kv_slice * D, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(prm.v + tk.kv_slice * D, (uint32_t)N * D * 2);
 
-  // key-tile ranges: workgroup (union over its rows) and this wave
-  auto tile_range = [&](int r0, int r1, int &lo, int &hi) {  // rows [r0, r1)
-    hi = prm.causal ? min(prm.nkt, (r1 - 1) / kBN + 1) : prm.nkt;
-    lo = prm.window > 0 ? max(0, r0 - prm.window + 1) / kBN : 0;
-  };
-  int wg_lo, wg_hi, w_lo, w_hi;
-  tile_range(wg_r0, min(N, wg_r0 + kRows), wg_lo, wg_hi);
-  if (qw0 < N) {
-    tile_range(qw0, min(N, qw0 + 32), w_lo, w_hi);
-  } else {
-    w_lo = w_hi = 0;  // rows past the end: this wave only helps load tiles
-  }
-
-  // every wave of the workgroup reads the same KV head (P divides G)
-  const size_t kv_slice = (size_t)(b * prm.Hkv + kvh) * N * D;
-  const size_t q_slice = (size_t)(b * prm.Hq + head) * N * D;
-  const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(prm.k + kv_slice, (uint32_t)N * D * 2);
-  const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(prm.v + kv_slice, (uint32_t)N * D * 2);
-
-  // ---- Q^T operand: lane holds query row qw0 + l32, d = 16*kk + 8*hh + s
   bf16x8 qf[g::kKSteps];
-  {
-    const int row = qw0 + l32;
-    const uint16_t *qp = prm.q + q_slice + (size_t)row * D + 8 * hh;
-#pragma unroll
-    for (int kk = 0; kk < g::kKSteps; ++kk) {
-      if (row < N) {
-        qf[kk] = *(const bf16x8 *)(qp + 16 * kk);
-      } else {
-        qf[kk] = bf16x8{};
-      }
-      if (prm.neg) {
-        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-        u32x4 t = __builtin_bit_cast(u32x4, qf[kk]);
-        t ^= 0x80008000u;
-        qf[kk] = __builtin_bit_cast(bf16x8, t);
-      }
-    }
-  }
-
-  // per-lane LDS byte offsets
-  // K (b128): key row 32*rb + l32, d = 16*kk + 8*hh .. +7
-  const int k_lane = l32 * g::kKStride + hh * 16;
-  // V (transposed read): key row 32rb + 16tt + 8u + 4hh + (lane & 15) / 4,
-  // d = 32db + 16*((lane >> 4) & 1) + 4*(lane & 3) .. +3
-  const int v_lane = (4 * hh + ((lane & 15) >> 2)) * g::kVStride +
-                     (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  load_q<D>(prm, tk, l32, hh, qf);
+  const int k_lane = k_lane_off<D>(lane);
+  const int v_lane = v_lane_off<D>(lane);
 
   f32x16 oacc[g::kDB];
 #pragma unroll
   for (int i = 0; i < g::kDB; ++i) oacc[i] = f32x16{};
-  float m2 = -1e30f;   // running max, scaled log2 units (finite: no inf - inf)
-  float lsum = 0.0f;   // this lane's partial row sum (its 32 of every 64 keys)
-  float lrnd = 0.0f;   // the same over the bf16-rounded weights
+  RowState st;
   const float c = prm.c;
 
   TileStage<D, NW> stage;
-  if (wg_lo < wg_hi) {
-    stage.load(rs_k, rs_v, wg_lo * kBN, tid);
-    stage.store(set0, tid);
+  if (tk.wg_lo < tk.wg_hi) {
+    stage.load(rs_k, rs_v, tk.wg_lo * kBN, tk.wg_lo * kBN, tid);
+    stage.store(set0, set0 + g::kKTileB, tid);
   }
   __syncthreads();
 
   // S^T, mask, online softmax and O^T update for key tile t held in `set`.
   auto compute = [&](const int t, const lchar *const set) {
-
-    const int j0 = t * kBN;
     const lchar *kb = set + k_lane;
     const lchar *vb = set + g::kKTileB + v_lane;
-
-    // LDS fragment readers.  K fragment (kk, rb): key row 32*rb + l32, d
-    // chunk 2*kk + hh.  V^T fragment i of the PV sequence (db = i / 4,
-    // rb = (i / 2) % 2, tt = i % 2): two transposed reads of 4 keys each.
-    auto kfrag = [&](int kk, int rb) -> bf16x8 {
-      return *(const lds_bf16x8_t *)(kb + rb * 32 * g::kKStride + kk * 32);
-    };
-    auto vfrag = [&](int i) -> bf16x8 {
-      const int db = i >> 2, rb = (i >> 1) & 1, tt = i & 1;
-      i16x4 half[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int off = (32 * rb + 16 * tt + 8 * u) * g::kVStride + db * 64;
-        half[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vb + off));
-      }
-      typedef short i16x8 __attribute__((ext_vector_type(8)));
-      const i16x8 both = {half[0][0], half[0][1], half[0][2], half[0][3],
-                          half[1][0], half[1][1], half[1][2], half[1][3]};
-      return __builtin_bit_cast(bf16x8, both);
-    };
-    constexpr int kPV = 4 * g::kDB;  // PV MFMAs per tile
-    constexpr int kKA = 3;           // K ring depth (k-steps in flight)
-    constexpr int kVA = 4;           // V ring depth (MFMAs in flight)
+    constexpr int kKA = 3;  // K ring depth (k-steps in flight)
+    constexpr int kVA = 4;  // V ring depth (MFMAs in flight)
 
     // ---- S^T = K Q^T for 64 keys x 32 queries; K reads run kKA-1 k-steps
     // ahead of the MFMAs that consume them (sched_barrier fences keep the
@@ -293,120 +453,41 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
     bf16x8 ka[kKA][2];
 #pragma unroll
     for (int kk = 0; kk < kKA - 1; ++kk) {
-      ka[kk][0] = kfrag(kk, 0);
-      ka[kk][1] = kfrag(kk, 1);
+      ka[kk][0] = kfrag<D>(kb, kk, 0);
+      ka[kk][1] = kfrag<D>(kb, kk, 1);
     }
 #pragma unroll
     for (int kk = 0; kk < g::kKSteps; ++kk) {
       if (kk + kKA - 1 < g::kKSteps) {
-        ka[(kk + kKA - 1) % kKA][0] = kfrag(kk + kKA - 1, 0);
-        ka[(kk + kKA - 1) % kKA][1] = kfrag(kk + kKA - 1, 1);
+        ka[(kk + kKA - 1) % kKA][0] = kfrag<D>(kb, kk + kKA - 1, 0);
+        ka[(kk + kKA - 1) % kKA][1] = kfrag<D>(kb, kk + kKA - 1, 1);
       }
       __builtin_amdgcn_sched_barrier(0);
       s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % kKA][0], qf[kk], s[0], 0, 0, 0);
       s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % kKA][1], qf[kk], s[1], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // the first V^T fragments do not depend on P: start them now so the
-    // softmax hides their latency
+    // The V^T fragment sequence of the PV MFMAs: i -> (db, rb, tt) =
+    // (i / 4, (i / 2) % 2, i % 2).  The first ones do not depend on P:
+    // start them now so the softmax hides their latency.
+    auto vf = [&](int i) { return vfrag<D>(vb, i >> 2, (i >> 1) & 1, i & 1); };
     bf16x8 va[kVA];
 #pragma unroll
-    for (int i = 0; i < kVA; ++i) va[i] = vfrag(i);
+    for (int i = 0; i < kVA; ++i) va[i] = vf(i);
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- mask: only tiles that hold a masked (row, key) pair for this wave
-    const bool need_mask = (prm.causal && j0 + kBN - 1 > qw0) ||
-                           (prm.window > 0 && j0 <= qw0 + 31 - prm.window) || (j0 + kBN > N);
-    if (need_mask) {
-      // Register r of block rb holds key kbase + off with the compile-time
-      // off = 32*rb + 8*(r/4) + r%4.  The keys this lane's row sees form the
-      // range lo < off <= hi relative to kbase, so one unsigned compare per
-      // register decides visibility: (unsigned)(off - lo - 1) < hi - lo.
-      const int qrow = qw0 + l32;
-      const int kbase = j0 + 4 * hh;
-      int hi = N - 1 - kbase;
-      if (prm.causal) hi = min(hi, qrow - kbase);
-      const int lo = prm.window > 0 ? qrow - prm.window - kbase : -1 - kbase;
-      const unsigned span = (unsigned)max(hi - lo, 0);
-      const int lo1 = lo + 1;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = 32 * rb + 8 * (r >> 2) + (r & 3);
-          const bool vis = (unsigned)(off - lo1) < span;
-          s[rb][r] = vis ? s[rb][r] : -INFINITY;
-        }
-      }
-    }
-
-    // ---- online softmax (scaled log2 domain)
-    float mx = s[0][0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = wave_max_pair(mx);
-    const float mt2 = mx * c;
-    // Lazy rescale: the reference point m2 only moves (and O is rescaled)
-    // when some row's tile max exceeds it by more than kTau (log2 units), so
-    // P <= 2^kTau; most tiles skip the 64 multiplies.  When it moves, every
-    // row of the wave takes its exact running max.
-    const bool grow = mt2 > m2 + kTau;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float mnew = fmaxf(m2, mt2);
-      const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
-      lsum *= alpha;
-      lrnd *= alpha;
-#pragma unroll
-      for (int i = 0; i < g::kDB; ++i) oacc[i] *= alpha;
-      m2 = mnew;
-    }
-    const float negm = -m2;
+    mask_tile(s, prm, t * kBN, tk.qw0, l32, hh);
     bf16x8 pf[2][2];
-    float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent add chains
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][8 * tt + e], c, negm));
-          part[e & 3] += p;
-          pf[rb][tt][e] = (__bf16)p;
-        }
-      }
-    }
-    lsum += (part[0] + part[1]) + (part[2] + part[3]);
-    // The same weights as the PV MFMA sees them (bf16), summed with
-    // v_dot2_f32_bf16 against (1, 1): normalizing O by this sum makes a row
-    // dominated by one key return that key's V row up to fp32 rounding, even
-    // when its weight is not exactly 1.0 (lazy rescale).
-    {
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-      float rp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bf16x2 pair = {pf[rb][tt][2 * e], pf[rb][tt][2 * e + 1]};
-            rp[e] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, rp[e], false);
-          }
-        }
-      }
-      lrnd += (rp[0] + rp[1]) + (rp[2] + rp[3]);
-    }
+    softmax_tile<g::kDB>(s, pf, st, oacc, c);
 
     // ---- O^T += V^T P^T; V reads run kVA MFMAs ahead
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < kPV; ++i) {
+    for (int i = 0; i < g::kPV; ++i) {
       const int db = i >> 2, rb = (i >> 1) & 1, tt = i & 1;
       const bf16x8 a = va[i % kVA];
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[rb][tt], oacc[db], 0, 0, 0);
-      if (i + kVA < kPV) va[i % kVA] = vfrag(i + kVA);
+      if (i + kVA < g::kPV) va[i % kVA] = vf(i + kVA);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -416,39 +497,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
   // in the other buffer set.  The register loads are only waited for at that
   // final store, so they overlap the whole tile's compute.
   auto step = [&](const int t, lchar *const cur_set, lchar *const next_set) {
-    const bool more = t + 1 < wg_hi;
-    if (more) stage.load(rs_k, rs_v, (t + 1) * kBN, tid);
-    if (t >= w_lo && t < w_hi) compute(t, cur_set);
-    if (more) stage.store(next_set, tid);
+    const bool more = t + 1 < tk.wg_hi;
+    if (more) stage.load(rs_k, rs_v, (t + 1) * kBN, (t + 1) * kBN, tid);
+    if (t >= tk.w_lo && t < tk.w_hi) compute(t, cur_set);
+    if (more) stage.store(next_set, next_set + g::kKTileB, tid);
     __syncthreads();
   };
 
-  for (int t = wg_lo; t < wg_hi; t += 2) {
+  for (int t = tk.wg_lo; t < tk.wg_hi; t += 2) {
     step(t, set0, set1);
-    if (t + 1 < wg_hi) step(t + 1, set1, set0);
+    if (t + 1 < tk.wg_hi) step(t + 1, set1, set0);
   }
 
-  // ---- epilogue: O = O / l (bf16, RNE), lse = ln(sum) + max
-  const float ltot = wave_sum_pair(lsum);
-  const float lrtot = wave_sum_pair(lrnd);
-  const int row = qw0 + l32;
-  if (row < N) {
-    const float inv = 1.0f / lrtot;
-    uint16_t *op = prm.o + q_slice + (size_t)row * D + 4 * hh;
-#pragma unroll
-    for (int db = 0; db < g::kDB; ++db) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bf16x4 w;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = (__bf16)(oacc[db][4 * i + j] * inv);
-        *(bf16x4 *)(op + 32 * db + 8 * i) = w;
-      }
-    }
-    if (hh == 0) {
-      prm.lse[(size_t)(b * prm.Hq + head) * N + row] = (m2 + __builtin_amdgcn_logf(ltot)) * kLn2;
-    }
-  }
+  write_out<D>(prm, tk, l32, hh, oacc, st);
 }
 
 template <int D, int NW, int P>
@@ -488,6 +549,11 @@ hipError_t launch_nw(const FwdProblem &p, hipStream_t stream) {
   return launch_t<D, NW, 1>(p, stream);
 }
 
+template <int D>
+hipError_t launch_d(const FwdProblem &p, int v, hipStream_t stream) {
+  return v == kWaves4 ? launch_nw<D, 4>(p, stream) : launch_nw<D, 8>(p, stream);
+}
+
 }  // namespace
 
 const char *variant_name(int variant) {
@@ -501,10 +567,7 @@ const char *variant_name(int variant) {
 
 hipError_t launch_fwd(const FwdProblem &p, int variant, hipStream_t stream) {
   const int v = variant == kAuto ? kWaves8 : variant;
-  if (p.d == 128) {
-    return v == kWaves4 ? launch_nw<128, 4>(p, stream) : launch_nw<128, 8>(p, stream);
-  }
-  return v == kWaves4 ? launch_nw<64, 4>(p, stream) : launch_nw<64, 8>(p, stream);
+  return p.d == 128 ? launch_d<128>(p, v, stream) : launch_d<64>(p, v, stream);
 }
 
 }  // namespace attn

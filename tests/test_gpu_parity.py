@@ -86,7 +86,10 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("variant", [1, 2])
+VARIANTS = [1, 2]  # every explicit kernel variant
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
 def test_parity_small_shapes(shape, variant):
     B, Hq, Hkv, N, d, causal, window = shape
@@ -101,9 +104,10 @@ def test_parity_small_shapes(shape, variant):
 def test_variants_agree():
     q, k, v = make_qkv(1, 8, 2, 700, 128, seed=5)
     a = run(q, k, v, True, 300, variant=1)
-    b = run(q, k, v, True, 300, variant=2)
-    assert torch.equal(a[0], b[0]) or (a[0].float() - b[0].float()).abs().max() < 1e-2
-    assert (a[1] - b[1]).abs().max() < 1e-4
+    for var in VARIANTS[1:]:
+        b = run(q, k, v, True, 300, variant=var)
+        assert torch.equal(a[0], b[0]) or (a[0].float() - b[0].float()).abs().max() < 1e-2
+        assert (a[1] - b[1]).abs().max() < 1e-4
 
 
 # ---------------------------------------------------------------------------
@@ -289,19 +293,21 @@ def test_workload_parity(name):
           f"{name} ({len(rows_of(0))} rows/head)")
 
 
+@pytest.mark.parametrize("variant", [0])
 @pytest.mark.parametrize("name", ["c2_causal_mha", "c2_causal_mha_sharp", "c3_causal_window",
                                   "c4_causal_gqa"])
-def test_workload_parity_every_row(name):
+def test_workload_parity_every_row(name, variant):
     """The full-size launch checked on every row of every head: the oracle
     covers these workloads in seconds on the host cores, so the worst row
-    (not only a sample) must meet the bar."""
+    (not only a sample) must meet the bar.  The default variant, as
+    benchmarked."""
     w = WORKLOADS[name]
-    say(f"case workload {name} (every row)")
+    say(f"case workload {name} (every row) variant {variant}")
     q, k, v = _inputs(w)
-    o, lse = run(q, k, v, w.causal, w.window, scale=w.sm_scale)
+    o, lse = run(q, k, v, w.causal, w.window, scale=w.sm_scale, variant=variant)
     from threadpoolctl import threadpool_limits
     qf, kf, vf = q.float().numpy(), k.float().numpy(), v.float().numpy()
     with threadpool_limits(limits=1, user_api="blas"):
         o_ref, l_ref = attention_forward(qf, kf, vf, w.sm_scale, w.causal, w.window,
                                          workers=16)
-    check(o, lse, o_ref, l_ref, f"{name} (every row)")
+    check(o, lse, o_ref, l_ref, f"{name} (every row) v{variant}")
