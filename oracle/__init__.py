@@ -1,4 +1,5 @@
-"""CPU oracle for exact softmax attention forward -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for exact softmax attention (forward and gradients) -- TEST
+INFRASTRUCTURE ONLY.
 
 Only the test suite, the smoke check in the package entry file and the
 ``cpu_baseline`` leg of the bench script may import anything in this
@@ -13,6 +14,10 @@ Contents
                blocks restricted to each block's visible key span.
 ``brute``      Pure-Python double loops with ``math.fsum``, tiny shapes only;
                it pins ``attention``.
+``backward``   NumPy float64 gradients (dQ, dK, dV) of the same definition,
+               by the chain rule; pinned by central finite differences of the
+               forward oracle, by float64 autograd through masked SDPA and by
+               closed forms.
 
 What the oracle computes (the plain definition; every page agrees that the
 tiled method returns exactly this result):
@@ -45,4 +50,5 @@ from .attention import (  # noqa: F401
     kv_head_of,
     visible_span,
 )
+from .backward import attention_backward  # noqa: F401
 from .brute import brute_attention  # noqa: F401

@@ -47,7 +47,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 
-def _check(q, k, v, causal, window):
+def check_shapes(q, k, v, causal, window):
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("q, k, v must be (B, H, N, d)")
     B, Hq, N, d = q.shape
@@ -94,8 +94,12 @@ def _visible_mask(rows: np.ndarray, lo: int, hi: int, causal: bool, window: int)
     return allowed
 
 
-def _rows_block(qh, kh, vh, rows, sigma, causal, window, N):
-    """Exact attention for the given query rows of one (batch, head)."""
+def rows_probabilities(qh, kh, rows, sigma, causal, window, N):
+    """Softmax weights of the given query rows of one (batch, head).
+
+    Returns ``(p, lo, hi, lse)``: p is (len(rows), hi - lo) float64 over the
+    union key span [lo, hi) of the rows, exactly 0 where a key is masked.
+    """
     spans = [visible_span(int(i), N, causal, window) for i in rows]
     lo = min(s[0] for s in spans)
     hi = max(s[1] for s in spans)
@@ -109,11 +113,17 @@ def _rows_block(qh, kh, vh, rows, sigma, causal, window, N):
     l = e.sum(axis=1)
     lse = m[:, 0] + np.log(l)
     p = e / l[:, None]
+    return p, lo, hi, lse
+
+
+def _rows_block(qh, kh, vh, rows, sigma, causal, window, N):
+    """Exact attention for the given query rows of one (batch, head)."""
+    p, lo, hi, lse = rows_probabilities(qh, kh, rows, sigma, causal, window, N)
     o = p @ vh[lo:hi]
     return o, lse
 
 
-def _row_blocks(rows, N, causal, window, block):
+def row_blocks(rows, N, causal, window, block):
     """Cut ``rows`` into runs of at most ``block`` entries whose union key span
     stays within twice the widest single-row span (so scattered rows under a
     window are not multiplied against keys none of them can see)."""
@@ -140,7 +150,7 @@ def _row_blocks(rows, N, causal, window, block):
     return out
 
 
-def _as_f64(x):
+def as_f64(x):
     x = np.asarray(x)
     if x.dtype != np.float64:
         x = x.astype(np.float64)
@@ -166,7 +176,7 @@ def attention_rows(q, k, v, scale, causal=False, window=0, rows=None, block=256,
     R = len(rows).
     """
     q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
-    B, Hq, Hkv, N, d = _check(q, k, v, causal, window)
+    B, Hq, Hkv, N, d = check_shapes(q, k, v, causal, window)
     sigma = float(np.float32(scale))
     if not math.isfinite(sigma):
         raise ValueError("scale must be finite")
@@ -177,13 +187,13 @@ def attention_rows(q, k, v, scale, causal=False, window=0, rows=None, block=256,
     o = np.empty((B, Hq, R, d), dtype=np.float64)
     lse = np.empty((B, Hq, R), dtype=np.float64)
 
-    blocks = _row_blocks(rows, N, causal, window, block)
+    blocks = row_blocks(rows, N, causal, window, block)
 
     def one_slice(bh):
         b, h = divmod(bh, Hq)
         kvh = kv_head_of(h, Hq, Hkv)
         # widened one slice at a time so long inputs stay float32 in memory
-        qh, kh, vh = _as_f64(q[b, h]), _as_f64(k[b, kvh]), _as_f64(v[b, kvh])
+        qh, kh, vh = as_f64(q[b, h]), as_f64(k[b, kvh]), as_f64(v[b, kvh])
         for r0, r1 in blocks:
             sel = rows[r0:r1]
             ob, lb = _rows_block(qh, kh, vh, sel, sigma, causal, window, N)
