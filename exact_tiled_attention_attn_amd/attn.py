@@ -1,7 +1,7 @@
 """Python binding of libattn.so (ctypes).  Argument marshalling only.
 
-The names mirror include/attn.h.  Every step of the attention forward runs in
-the HIP library; PyTorch is used here for device memory and the current
+The names mirror include/attn.h.  Every step of the attention forward and
+backward runs in the HIP library; PyTorch is used here for device memory and the current
 stream.  There is no fallback: if the library is missing or a call fails, an
 ``AttnError`` is raised.
 """
@@ -21,8 +21,8 @@ ATTN_ERR_UNSUPPORTED = 2
 ATTN_ERR_LAUNCH = 3
 ATTN_MAX_N = 1 << 22
 
-EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_num_variants", "attn_variant_name",
-            "attn_status_string", "attn_abi_version")
+EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_bwd_workspace_size",
+            "attn_num_variants", "attn_variant_name", "attn_status_string", "attn_abi_version")
 
 
 class AttnError(RuntimeError):
@@ -50,6 +50,10 @@ def load_library():
     lib.attn_fwd.restype = i
     lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
     lib.attn_fwd_ex.restype = i
+    lib.attn_bwd.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, i, vp]
+    lib.attn_bwd.restype = i
+    lib.attn_bwd_workspace_size.argtypes = [i, i, i]
+    lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.attn_num_variants.argtypes = []
     lib.attn_num_variants.restype = i
     lib.attn_variant_name.argtypes = [i]
@@ -103,6 +107,23 @@ def attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, window, varian
                            int(variant), _stream(stream, q, k, v, o, lse))
 
 
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, scale, causal,
+             window, stream=None):
+    """Call the C backward entry point; returns its status code (0 = ATTN_OK).
+
+    Tensors or raw device addresses (int), as for attn_fwd.
+    """
+    lib = load_library()
+    return lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                        _ptr(dk), _ptr(dv), _ptr(workspace), int(B), int(Hq), int(Hkv), int(N),
+                        int(d), float(scale), int(causal), int(window),
+                        _stream(stream, q, k, v, o, lse, dout, dq, dk, dv))
+
+
+def attn_bwd_workspace_size(B, Hq, N):
+    return int(load_library().attn_bwd_workspace_size(int(B), int(Hq), int(N)))
+
+
 def attn_num_variants():
     return load_library().attn_num_variants()
 
@@ -151,3 +172,44 @@ def fwd(q, k, v, causal=False, window=0, scale=None, variant=0, out=None, stream
     if st != ATTN_OK:
         raise AttnError(f"attn_fwd failed: {attn_status_string(st)} (status {st})", st)
     return o, lse
+
+
+def bwd(q, k, v, o, lse, dout, causal=False, window=0, scale=None, out=None, workspace=None,
+        stream=None):
+    """Allocate (dq, dk, dv) and the workspace with torch and run the backward.
+
+    q, k, v, o, lse: as passed to / returned by ``fwd`` for the same
+    arguments; dout: (B, Hq, N, d) bf16.  Returns (dq, dk, dv) in bf16 with
+    the shapes of q, k and v.  Raises on any error.
+    """
+    import torch
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
+                        ("v", v, torch.bfloat16), ("o", o, torch.bfloat16),
+                        ("dout", dout, torch.bfloat16), ("lse", lse, torch.float32)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise AttnError(f"{name} must be a CUDA (HIP) tensor")
+        if t.dtype != dt:
+            raise AttnError(f"{name} must be {dt}")
+        if not t.is_contiguous():
+            raise AttnError(f"{name} must be contiguous")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if (tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != tuple(k.shape)
+            or tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape)
+            or tuple(lse.shape) != (B, Hq, N)):
+        raise AttnError("shapes must be q, o, dout (B, Hq, N, d), k, v (B, Hkv, N, d), "
+                        "lse (B, Hq, N)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+    if workspace is None:
+        nbytes = attn_bwd_workspace_size(B, Hq, N)
+        workspace = torch.empty((max(nbytes, 4) // 4,), dtype=torch.float32, device=q.device)
+    st = attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, scale,
+                  int(bool(causal)), int(window), stream)
+    if st != ATTN_OK:
+        raise AttnError(f"attn_bwd failed: {attn_status_string(st)} (status {st})", st)
+    return dq, dk, dv

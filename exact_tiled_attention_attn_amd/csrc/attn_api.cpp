@@ -1,4 +1,4 @@
-// C ABI entry points: argument validation, then one kernel launch.
+// C ABI entry points: argument validation, then the kernel launches.
 //
 // Validation runs before any HIP call, so a rejected call launches nothing
 // and leaves o / lse untouched.  The rules follow the problem statement in
@@ -40,6 +40,19 @@ attn_status_t validate(const attn::FwdProblem &p, int variant) {
   return ATTN_OK;
 }
 
+attn_status_t validate_bwd(const attn::BwdProblem &p) {
+  const attn::FwdProblem f{p.q, p.k, p.v, const_cast<void *>(p.o), const_cast<float *>(p.lse),
+                           p.B, p.Hq, p.Hkv, p.N, p.d, p.scale, p.causal, p.window};
+  const attn_status_t st = validate(f, attn::kAuto);
+  if (st != ATTN_OK) return st;
+  if (p.B == 0 || p.N == 0) return ATTN_OK;
+  if (!p.dout || !p.dq || !p.dk || !p.dv || !p.delta) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(p.dout) || !aligned16(p.dq) || !aligned16(p.dk) || !aligned16(p.dv) ||
+      !aligned16(p.delta))
+    return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -63,6 +76,27 @@ attn_status_t attn_fwd(const void *q, const void *k, const void *v, void *o, flo
                        void *stream) {
   return attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, window, attn::kAuto,
                      stream);
+}
+
+size_t attn_bwd_workspace_size(int B, int Hq, int N) {
+  if (B <= 0 || Hq <= 0 || N <= 0) return 0;
+  return static_cast<size_t>(B) * static_cast<size_t>(Hq) * static_cast<size_t>(N) * sizeof(float);
+}
+
+attn_status_t attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                       const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                       void *workspace, int B, int Hq, int Hkv, int N, int d, float scale,
+                       int causal, int window, void *stream) {
+  attn::BwdProblem p{q,  k,  v,  o, dout, lse, static_cast<float *>(workspace), dq, dk, dv, B, Hq,
+                     Hkv, N, d, scale, causal, window};
+  const attn_status_t st = validate_bwd(p);
+  if (st != ATTN_OK) return st;
+  if (B == 0 || N == 0) return ATTN_OK;
+  if (p.window >= N) p.window = 0;
+  if (p.window < 0) p.window = 0;
+  const hipError_t e = attn::launch_bwd(p, static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidValue) return ATTN_ERR_UNSUPPORTED;
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 int attn_num_variants(void) { return attn::kNumVariants; }

@@ -1,5 +1,6 @@
 // Private interface between the C ABI entry points (attn_api.cpp) and the
-// gfx950 kernels (attn_fwd.hip).  Not installed, not part of the ABI.
+// gfx950 kernels (attn_fwd.hip, attn_bwd.hip).  Not installed, not part of
+// the ABI.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -29,5 +30,19 @@ const char *variant_name(int variant);
 // Enqueue the forward kernel for `p` on `stream`.  Returns the HIP status of
 // the launch call (hipSuccess when it was enqueued).
 hipError_t launch_fwd(const FwdProblem &p, int variant, hipStream_t stream);
+
+// One backward problem, already validated by the entry point.
+struct BwdProblem {
+  const void *q, *k, *v, *o, *dout;
+  const float *lse;
+  float *delta;  // workspace, B * Hq * N floats
+  void *dq, *dk, *dv;
+  int B, Hq, Hkv, N, d;
+  float scale;
+  int causal, window;  // window <= 0: none
+};
+
+// Enqueue the three backward kernels (Delta, dQ, dK/dV) for `p` on `stream`.
+hipError_t launch_bwd(const BwdProblem &p, hipStream_t stream);
 
 }  // namespace attn

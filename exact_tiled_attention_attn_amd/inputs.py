@@ -10,6 +10,9 @@ Q, K, V are i.i.d. N(0, 1) draws in float32 from
 inside each tensor, one (N, d) slice per (batch, head) in row-major order,
 then rounded to bfloat16 with round-to-nearest-even (``Tensor.to``).  The
 per-slice drawing keeps host memory bounded at the longest shapes.
+
+The upstream gradient dO of the backward is drawn the same way, from its own
+seed, as one (B, Hq, N, d) tensor of N(0, 1) values rounded to bfloat16.
 """
 
 from __future__ import annotations
@@ -34,6 +37,12 @@ def make_qkv(B: int, Hq: int, Hkv: int, N: int, d: int, seed: int):
     k = _draw(gen, B, Hkv, N, d)
     v = _draw(gen, B, Hkv, N, d)
     return q, k, v
+
+
+def make_dout(B: int, Hq: int, N: int, d: int, seed: int) -> torch.Tensor:
+    """Return a bf16 CPU tensor dO shaped (B, Hq, N, d)."""
+    gen = torch.Generator().manual_seed(int(seed))
+    return _draw(gen, B, Hq, N, d)
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:

@@ -1,5 +1,6 @@
 /*
- * attn.h -- C ABI of the MI355X (gfx950) exact tiled attention forward.
+ * attn.h -- C ABI of the MI355X (gfx950) exact tiled attention: the forward
+ * pass and its gradients.
  *
  * Operation.  For every batch b, query head h and query row i
  *
@@ -47,6 +48,8 @@
 #ifndef EXACT_TILED_ATTN_H
 #define EXACT_TILED_ATTN_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -93,6 +96,49 @@ attn_status_t attn_fwd_ex(const void *q, const void *k, const void *v, void *o, 
                           int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                           int window, int variant, void *stream);
 
+/* Backward pass: the gradients of a loss L with respect to q, k and v, given
+ * dout = dL/do for the forward above.  "Efficient attention: long context
+ * and sub-quadratic variants" (section "Against the real libraries") pairs
+ * the exact forward with a recompute-based backward; the result is the
+ * gradient of the forward definition, by the chain rule:
+ *
+ *     p_ij   = exp(s_ij - lse_i)                (recomputed from q, k, lse)
+ *     D_i    = sum_c dout[i,c] * o[i,c]
+ *     ds_ij  = p_ij * (<dout[i,:], v[j,:]> - D_i)
+ *     dq[i]  = scale * sum_j ds_ij k[j]
+ *     dk[j]  = scale * sum_i ds_ij q[i]         (summed over the query heads
+ *     dv[j]  =         sum_i p_ij dout[i]        that share the KV head)
+ *
+ * (masked pairs have p = ds = 0).  The shared-KV-head sum follows from the
+ * repeat_interleave of the KV heads ("Attention Mechanism Variants Beyond
+ * Self-Attention", section "Multi-Query and Grouped-Query Attention").
+ *
+ *   q, k, v, o, lse   the forward's inputs and outputs (o bf16, lse fp32 as
+ *                     written by attn_fwd for the same arguments)
+ *   dout              bf16 [B][Hq][N][d]
+ *   dq                bf16 [B][Hq][N][d]   written
+ *   dk, dv            bf16 [B][Hkv][N][d]  written (every row, also rows
+ *                                          no query sees)
+ *   workspace         device memory of attn_bwd_workspace_size(B, Hq, N)
+ *                     bytes, 16-byte aligned; holds D between the kernels,
+ *                     contents on entry and exit unspecified
+ *   the rest          as for attn_fwd
+ * Outputs are rounded to nearest even from fp32 accumulators; the sums over
+ * j and i are formed in fp32 with the products p * dout and ds * q, ds * k
+ * rounded to bf16 (the matrix-core operand type) first.  dq, dk, dv and the
+ * workspace must not overlap each other or any input.  The call enqueues
+ * three kernels on `stream` and returns without synchronising.  Errors as for
+ * attn_fwd (also for dout, dq, dk, dv and workspace); B == 0 or N == 0 is a
+ * valid empty problem. */
+attn_status_t attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                       const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                       void *workspace, int B, int Hq, int Hkv, int N, int d, float scale,
+                       int causal, int window, void *stream);
+
+/* Bytes of workspace attn_bwd needs: B * Hq * N * 4 (0 for an empty or
+ * invalid shape).  The library never allocates it itself. */
+size_t attn_bwd_workspace_size(int B, int Hq, int N);
+
 /* Number of variant ids accepted by attn_fwd_ex (ids 0 .. n-1). */
 int attn_num_variants(void);
 
@@ -103,7 +149,7 @@ const char *attn_variant_name(int variant);
 const char *attn_status_string(attn_status_t status);
 
 /* ABI version of this header (incremented on any signature change). */
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 int attn_abi_version(void);
 
 #ifdef __cplusplus

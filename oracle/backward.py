@@ -51,7 +51,7 @@ def attention_backward(q, k, v, do, scale, causal=False, window=0, block=256, wo
     scale, causal, window : as for the forward (the float32 value of scale
         is used, widened).
     block : query rows per block.
-    workers : thread-pool size over (batch, KV head) groups.
+    workers : thread-pool size over (batch, query head) pairs.
 
     Returns ``(dq, dk, dv)`` in float64 with the shapes of q, k and v.
     """
@@ -69,29 +69,36 @@ def attention_backward(q, k, v, do, scale, causal=False, window=0, block=256, wo
     rows = np.arange(N)
     blocks = row_blocks(rows, N, causal, window, block)
 
-    def one_group(bk):
-        # one (batch, KV head): its G query heads write disjoint dq slices and
-        # accumulate into this group's own dk, dv slices
-        b, kvh = divmod(bk, Hkv)
+    def one_head(bh):
+        # one (batch, query head): writes its own dq slice and returns its
+        # contributions to its KV head's dk and dv
+        b, h = divmod(bh, Hq)
+        kvh = h // G
         kh, vh = as_f64(k[b, kvh]), as_f64(v[b, kvh])
-        for h in range(kvh * G, (kvh + 1) * G):
-            qh, doh = as_f64(q[b, h]), as_f64(do[b, h])
-            for r0, r1 in blocks:
-                sel = rows[r0:r1]
-                p, lo, hi, _ = rows_probabilities(qh, kh, sel, sigma, causal, window, N)
-                dos = doh[sel]
-                o = p @ vh[lo:hi]
-                delta = np.einsum("ij,ij->i", dos, o)
-                dv[b, kvh, lo:hi] += p.T @ dos
-                dp = dos @ vh[lo:hi].T
-                ds = p * (dp - delta[:, None])
-                dq[b, h, sel] = sigma * (ds @ kh[lo:hi])
-                dk[b, kvh, lo:hi] += sigma * (ds.T @ qh[sel])
+        qh, doh = as_f64(q[b, h]), as_f64(do[b, h])
+        dkh = np.zeros((N, d), dtype=np.float64)
+        dvh = np.zeros((N, d), dtype=np.float64)
+        for r0, r1 in blocks:
+            sel = rows[r0:r1]
+            p, lo, hi, _ = rows_probabilities(qh, kh, sel, sigma, causal, window, N)
+            dos = doh[sel]
+            o = p @ vh[lo:hi]
+            delta = np.einsum("ij,ij->i", dos, o)
+            dvh[lo:hi] += p.T @ dos
+            dp = dos @ vh[lo:hi].T
+            ds = p * (dp - delta[:, None])
+            dq[b, h, sel] = sigma * (ds @ kh[lo:hi])
+            dkh[lo:hi] += sigma * (ds.T @ qh[sel])
+        return dkh, dvh
 
     if workers <= 1:
-        for bk in range(B * Hkv):
-            one_group(bk)
+        parts = [one_head(bh) for bh in range(B * Hq)]
     else:
         with ThreadPoolExecutor(max_workers=workers) as ex:
-            list(ex.map(one_group, range(B * Hkv)))
+            parts = list(ex.map(one_head, range(B * Hq)))
+    # the G query heads of a KV head add up in head order
+    for bh, (dkh, dvh) in enumerate(parts):
+        b, h = divmod(bh, Hq)
+        dk[b, h // G] += dkh
+        dv[b, h // G] += dvh
     return dq, dk, dv

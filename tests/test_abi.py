@@ -123,3 +123,48 @@ def test_fwd_wrapper_rejects_host_tensors(lib):
     q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
     with pytest.raises(attn.AttnError):
         attn.fwd(q, q, q)
+
+
+BWD_GOOD = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, workspace=P, B=1, Hq=4,
+                Hkv=2, N=64, d=128, scale=0.1, causal=1, window=0)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(o=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(lse=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(dout=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(dq=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(dk=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(dv=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(workspace=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(B=-1), attn.ATTN_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_INVALID_ARG),
+    (dict(causal=3), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), attn.ATTN_ERR_INVALID_ARG),
+    (dict(d=32), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(causal=0, window=8), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(dv=P + 2), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(workspace=P + 4), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(N=(1 << 22) + 1), attn.ATTN_ERR_UNSUPPORTED),
+])
+def test_bwd_rejects_bad_arguments_without_launching(lib, kw, expect):
+    a = dict(BWD_GOOD)
+    a.update(kw)
+    assert attn.attn_bwd(**a) == expect
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=0),
+                                dict(N=0, q=0, k=0, v=0, o=0, lse=0, dout=0, dq=0, dk=0, dv=0,
+                                     workspace=0)])
+def test_bwd_empty_problem_is_ok_and_launches_nothing(lib, kw):
+    a = dict(BWD_GOOD)
+    a.update(kw)
+    assert attn.attn_bwd(**a) == attn.ATTN_OK
+
+
+def test_bwd_workspace_size(lib):
+    assert attn.attn_bwd_workspace_size(2, 32, 8192) == 2 * 32 * 8192 * 4
+    assert attn.attn_bwd_workspace_size(0, 32, 8192) == 0
+    assert attn.attn_bwd_workspace_size(1, 1, -3) == 0
+    assert attn.attn_bwd_workspace_size(3, 64, 1 << 22) == 3 * 64 * (1 << 22) * 4
