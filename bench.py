@@ -8,6 +8,10 @@ already resident in HBM.  Throughput counts 4*d FLOPs per unmasked score
 ("Efficient attention: long context and sub-quadratic variants", section
 "The quadratic wall, stated concretely"), never the masked entries a tile
 computes and discards.  Prints one JSON line.
+
+The same line also carries the backward (attn_bwd: dQ, dK, dV) timed on the
+same workload, at 10*d FLOPs per unmasked score (S, dP, dV, dQ, dK: five
+2*d contractions), as a secondary figure.
 """
 
 from __future__ import annotations
@@ -27,6 +31,7 @@ METRIC = "attention fwd TFLOP/s (bf16, d=128, causal/window) and % of MFMA peak"
 MAIN = "c2_causal_mha"
 OTHERS = ["c2_causal_mha_sharp", "c3_causal_window", "c4_causal_gqa", "c5_long_causal",
           "c5_long_window"]
+BWD_OTHERS = ["c4_causal_gqa"]
 KERNEL_SRC = os.path.join(ROOT, "exact_tiled_attention_attn_amd", "csrc", "attn_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -92,6 +97,44 @@ def time_workload(w, steps, warmup, variant, torch, attn):
     ev_ms = e0.elapsed_time(e1) / steps
     del q, k, v, o, lse
     return wall_ms, ev_ms, host
+
+
+def time_backward(w, steps, warmup, torch, attn):
+    """attn_bwd (Delta, dQ, dK/dV kernels) on the workload, with o and lse
+    from attn_fwd.  Returns event ms per call."""
+    from exact_tiled_attention_attn_amd.inputs import make_dout
+    q, k, v, _ = device_inputs(w, torch)
+    do = make_dout(w.B, w.Hq, w.N, w.d, w.seed + 100).to(q.device)
+    o, lse = attn.fwd(q, k, v, causal=w.causal, window=w.window, scale=w.sm_scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty((attn.attn_bwd_workspace_size(w.B, w.Hq, w.N) // 4,), dtype=torch.float32,
+                     device=q.device)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        st = attn.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, w.B, w.Hq, w.Hkv, w.N, w.d,
+                           w.sm_scale, int(w.causal), w.window, stream)
+        if st != 0:
+            raise RuntimeError(f"attn_bwd: {attn.attn_status_string(st)}")
+
+    t_end = time.perf_counter() + 0.5
+    n = 0
+    while n < warmup or time.perf_counter() < t_end:
+        launch()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ev_ms = e0.elapsed_time(e1) / steps
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    return ev_ms
 
 
 def cpu_baseline(w, host, seconds):
@@ -194,6 +237,7 @@ def main():
     ap.add_argument("--workload", default=MAIN)
     ap.add_argument("--no-others", action="store_true", help="time only the main workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
@@ -208,7 +252,7 @@ def main():
 
     from exact_tiled_attention_attn_amd import attn
     from exact_tiled_attention_attn_amd.workloads import (MI355X_BF16_DENSE_TFLOPS, WORKLOADS,
-                                                          algorithmic_bytes, flops)
+                                                          algorithmic_bytes, bwd_flops, flops)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
@@ -279,6 +323,19 @@ def main():
                             "ms": round(em, 4), "steps": steps}
             torch.cuda.empty_cache()
         out["other_workloads"] = others
+    if not args.no_bwd:
+        bw = {}
+        for name in [w.name] + ([] if args.no_others else BWD_OTHERS):
+            bwl = WORKLOADS[name]
+            log(f"timing backward {name}")
+            em = time_backward(bwl, max(3, args.steps // 2), max(1, args.warmup // 2), torch,
+                               attn)
+            bf = bwd_flops(bwl)
+            bw[name] = {"tflops": round(bf / (em * 1e-3) / 1e12, 2),
+                        "pct_of_peak": round(100 * bf / (em * 1e-3) / 1e12 / peak, 2),
+                        "ms": round(em, 4), "flops_per_call": bf}
+            torch.cuda.empty_cache()
+        out["backward"] = bw
     if not args.no_cpu:
         log(f"oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)

@@ -37,6 +37,7 @@
 #include <cfloat>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "attn_device.h"
 #include "attn_internal.h"
@@ -60,10 +61,8 @@ struct BwdParams {
   int total;      // workgroups of the kernel being launched
   int nkt;        // key tiles of 64 (dQ kernel) = query tiles of 64 (dK/dV kernel)
   int nkb;        // dK/dV kernel: key blocks per (batch, KV head)
-  float c;        // |scale| * log2(e), at least FLT_MIN
-  float scale;    // dQ = scale * dS K
-  float ascale;   // |scale|: dK = |scale| * dS^T Q' with Q' = sign(scale) Q
-  int neg;        // scale < 0: Q is negated on load (exact in bf16)
+  float c;        // scale * log2(e): P = exp2(c <q, k> - lse * log2(e))
+  float scale;    // dQ = scale * dS K, dK = scale * dS^T Q
   int causal;
   int window;     // 0: none
 };
@@ -103,14 +102,15 @@ struct PairStage {
   static_assert(kLoads * NT == kBN * st::kCh, "tile must split evenly over the threads");
   u32x4 a[kLoads], b[kLoads];
 
+  // Issues the loads only: nothing here consumes the data, so the wave
+  // does not wait for it before the tile computed meanwhile.
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                       int row0, int tid, bool neg_a) {
+                                       int row0, int tid) {
 #pragma unroll
     for (int n = 0; n < kLoads; ++n) {
       const int off = row0 * st::kRowB + (n * NT + tid) * 16;
       a[n] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
       b[n] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
-      if (neg_a) a[n] ^= 0x80008000u;
     }
   }
   // Tensor a into tile a1 (stride S1) and tile a2 (stride S2); tensor b into
@@ -160,11 +160,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(BwdParams prm) 
   bf16x8 qf[st::kKSteps], of[st::kKSteps];
 #pragma unroll
   for (int kk = 0; kk < st::kKSteps; ++kk) {
-    qf[kk] = row_frag<D>(prm.q + tk.q_slice * D, row, N, 16 * kk + 8 * hh, prm.neg);
+    qf[kk] = row_frag<D>(prm.q + tk.q_slice * D, row, N, 16 * kk + 8 * hh, false);
     of[kk] = row_frag<D>(prm.dout + tk.q_slice * D, row, N, 16 * kk + 8 * hh, false);
   }
   const float lse2 = row < N ? prm.lse[tk.q_slice + row] * kLog2e : 0.0f;
   const float delta = row < N ? prm.delta[tk.q_slice + row] : 0.0f;
+#pragma unroll
+  for (int kk = 0; kk < st::kKSteps; ++kk) {
+    settle(qf[kk]);
+    settle(of[kk]);
+  }
+  settle(lse2);
+  settle(delta);
   const float c = prm.c;
 
   const int kb_lane = b128_lane_off<st::kB128>(lane);
@@ -179,12 +186,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(BwdParams prm) 
     stage.template store<st::kB128, st::kTr, false>(set, set + kKb, set + kKb + kKt, set, tid);
   };
   if (tk.wg_lo < tk.wg_hi) {
-    stage.load(rs_k, rs_v, tk.wg_lo * kBN, tid, false);
+    stage.load(rs_k, rs_v, tk.wg_lo * kBN, tid);
     put((lchar *)smem);
   }
   __syncthreads();
 
-  auto compute = [&](int t, const lchar *set) {
+  // edge mask: key j is visible from this lane's row iff
+  // (unsigned)(j - m_lo) < m_span
+  const int m_lo = prm.window > 0 ? max(0, row - prm.window + 1) : 0;
+  const int m_span = row < N ? (prm.causal ? row : N - 1) - m_lo + 1 : 0;
+
+  auto compute = [&](int t, const lchar *set, auto &&store_next) {
     const lchar *kb = set + kb_lane;
     const lchar *kt = set + kKb + kt_lane;
     const lchar *vb = set + kKb + kKt + kb_lane;
@@ -193,11 +205,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(BwdParams prm) 
                            (prm.window > 0 && j0 <= tk.qw0 + 31 - prm.window) || (j0 + kBN > N);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      // S^T (32 keys x 32 queries) and dP^T - Delta
-      f32x16 s = f32x16{};
-      f32x16 dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dp[r] = -delta;
+      // the next tile's LDS stores go out between the two key blocks, when
+      // its loads have had half the tile to land
+      if (rb == 1) store_next();
+      // S^T and dP^T (32 keys x 32 queries)
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < st::kKSteps; ++kk) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b128_frag<st::kB128>(kb, kk, rb), qf[kk], s,
@@ -206,19 +218,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(BwdParams prm) 
                                                      dp, 0, 0, 0);
       }
       // register r holds key j0 + 32 rb + 8 (r / 4) + 4 hh + r % 4
+      f32x16 p;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
+      if (need_mask) {
+        const int base = j0 + 32 * rb + 4 * hh - m_lo;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          p[r] = (unsigned)(base + 8 * (r >> 2) + (r & 3)) < (unsigned)m_span ? p[r] : 0.0f;
+      }
       bf16x8 dsf[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
-        if (need_mask) {
-          const int key = j0 + 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          bool vis = key < N && row < N;
-          if (prm.causal) vis = vis && key <= row;
-          if (prm.window > 0) vis = vis && key > row - prm.window;
-          p = vis ? p : 0.0f;
-        }
-        dsf[r >> 3][r & 7] = (__bf16)(p * dp[r]);
-      }
+      for (int r = 0; r < 16; ++r) dsf[r >> 3][r & 7] = (__bf16)(p[r] * (dp[r] - delta));
       // dQ^T += K^T dS^T
 #pragma unroll
       for (int db = 0; db < st::kDB; ++db) {
@@ -235,9 +246,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(BwdParams prm) 
   lchar *const set1 = (lchar *)smem + kSet;
   auto step = [&](int t, const lchar *cur, lchar *next) {
     const bool more = t + 1 < tk.wg_hi;
-    if (more) stage.load(rs_k, rs_v, (t + 1) * kBN, tid, false);
-    if (t >= tk.w_lo && t < tk.w_hi) compute(t, cur);
-    if (more) put(next);
+    if (more) stage.load(rs_k, rs_v, (t + 1) * kBN, tid);
+    auto store_next = [&]() {
+      if (more) put(next);
+    };
+    if (t >= tk.w_lo && t < tk.w_hi) {
+      compute(t, cur, store_next);
+    } else {
+      store_next();
+    }
     __syncthreads();
   };
   for (int t = tk.wg_lo; t < tk.wg_hi; t += 2) {
@@ -287,6 +304,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkdv_kernel(BwdParams prm
     kf[kk] = row_frag<D>(prm.k + kv_slice * D, key, N, 16 * kk + 8 * hh, false);
     vf[kk] = row_frag<D>(prm.v + kv_slice * D, key, N, 16 * kk + 8 * hh, false);
   }
+#pragma unroll
+  for (int kk = 0; kk < st::kKSteps; ++kk) {
+    settle(kf[kk]);
+    settle(vf[kk]);
+  }
 
   // query tiles the workgroup's keys and this wave's keys are seen from
   auto qrange = [&](int j_lo, int j_hi, int &lo, int &hi) {  // keys [j_lo, j_hi)
@@ -328,76 +350,109 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkdv_kernel(BwdParams prm
     const size_t q_slice = (size_t)(b * prm.Hq + h) * N;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(prm.q + q_slice * D, (uint32_t)N * D * 2);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(prm.dout + q_slice * D, (uint32_t)N * D * 2);
-    stage.load(rq, ro, qt * kBN, tid, prm.neg);
+    stage.load(rq, ro, qt * kBN, tid);
     const int i = qt * kBN + (tid & (kBN - 1));
-    val = row_val && i < N ? val_src[q_slice + i] * val_mul : 0.0f;
+    val = row_val && i < N ? val_src[q_slice + i] : 0.0f;
   };
   auto put = [&](lchar *set) {
     stage.template store<st::kB128, st::kTr, true>(set + kQb, set + kQt, set + kOb, set + kOt, tid);
     static_assert(kDel == kLse + 4 * kBN, "lse and Delta arrays must be adjacent");
-    if (row_val) ((lds_f32_t *)(set + kLse))[tid] = val;
+    if (row_val) ((lds_f32_t *)(set + kLse))[tid] = val * val_mul;
   };
 
-  auto compute = [&](int s, const lchar *set) {
-    const int qt = qlo + s % per_head;
+  // edge mask: query row i sees this lane's key iff (unsigned)(i - m_lo) < m_span
+  const int m_lo = prm.causal ? key : 0;
+  const int m_span = key >= N ? 0
+                     : !prm.causal ? N
+                     : prm.window > 0 ? min(prm.window, N - key) : N - key;
+
+  // S and dP (32 queries x 32 keys) of row block rb; register r holds query
+  // row 32 rb + 8 (r / 4) + 4 hh + r % 4 of the tile
+  auto sdp = [&](const lchar *set, int rb, f32x16 &sa, f32x16 &dp) {
     const lchar *qb = set + kQb + qb_lane;
-    const lchar *qtr = set + kQt + qt_lane;
     const lchar *ob = set + kOb + qb_lane;
+    sa = f32x16{};
+    dp = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < st::kKSteps; ++kk) {
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b128_frag<st::kB128>(qb, kk, rb), kf[kk], sa, 0,
+                                                   0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b128_frag<st::kB128>(ob, kk, rb), vf[kk], dp, 0,
+                                                   0, 0);
+    }
+  };
+  // P = exp2(S c - lse log2 e) (zero where masked) and dS = P (dP - Delta),
+  // as bf16 B operands
+  auto softmax = [&](auto masked, const lchar *set, int q0, int rb, const f32x16 &sa,
+                     const f32x16 &dp, bf16x8 (&pf)[2], bf16x8 (&dsf)[2]) {
+    const lds_f32x4_t *lsep = (const lds_f32x4_t *)(set + kLse) + 8 * rb + hh;
+    const lds_f32x4_t *delp = (const lds_f32x4_t *)(set + kDel) + 8 * rb + hh;
+    f32x16 p;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const f32x4 l2 = lsep[2 * a];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        p[4 * a + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[4 * a + e], c, -l2[e]));
+    }
+    if constexpr (decltype(masked)::value) {
+      const int base = q0 + 32 * rb + 4 * hh - m_lo;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        p[r] = (unsigned)(base + 8 * (r >> 2) + (r & 3)) < (unsigned)m_span ? p[r] : 0.0f;
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const f32x4 dl = delp[2 * a];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * a + e;
+        pf[r >> 3][r & 7] = (__bf16)p[r];
+        dsf[r >> 3][r & 7] = (__bf16)(p[r] * (dp[r] - dl[e]));
+      }
+    }
+  };
+  // dV^T += dO^T P, dK^T += Q^T dS over the 32 rows of block rb
+  auto dkdv = [&](const lchar *set, int rb, const bf16x8 (&pf)[2], const bf16x8 (&dsf)[2]) {
+    const lchar *qtr = set + kQt + qt_lane;
     const lchar *otr = set + kOt + qt_lane;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int q0 = qt * kBN + 32 * rb;  // first query row of this block
-      // register r holds query row q0 + 8 (r / 4) + 4 hh + r % 4
-      const lds_f32x4_t *lsep = (const lds_f32x4_t *)(set + kLse) + 8 * rb + hh;
-      const lds_f32x4_t *delp = (const lds_f32x4_t *)(set + kDel) + 8 * rb + hh;
-      f32x16 s_acc = f32x16{};
-      f32x16 dp;
+    for (int db = 0; db < st::kDB; ++db) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const f32x4 dl = delp[2 * a];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dp[4 * a + e] = -dl[e];
+      for (int tt = 0; tt < 2; ++tt) {
+        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<st::kTr>(otr, db, rb, tt),
+                                                            pf[tt], dvacc[db], 0, 0, 0);
+        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<st::kTr>(qtr, db, rb, tt),
+                                                            dsf[tt], dkacc[db], 0, 0, 0);
       }
-#pragma unroll
-      for (int kk = 0; kk < st::kKSteps; ++kk) {
-        s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b128_frag<st::kB128>(qb, kk, rb), kf[kk],
-                                                        s_acc, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b128_frag<st::kB128>(ob, kk, rb), vf[kk], dp,
-                                                     0, 0, 0);
-      }
-      const bool need_mask = (prm.causal && q0 < kw0 + 31) ||
-                             (prm.window > 0 && q0 + 31 >= kw0 + prm.window) ||
-                             (q0 + 31 >= N) || (kw0 + 31 >= N);
-      bf16x8 pf[2], dsf[2];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const f32x4 l2 = lsep[2 * a];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * a + e;
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r], c, -l2[e]));
-          if (need_mask) {
-            const int qrow = q0 + 8 * a + 4 * hh + e;
-            bool vis = key < N && qrow < N;
-            if (prm.causal) vis = vis && key <= qrow;
-            if (prm.window > 0) vis = vis && key > qrow - prm.window;
-            p = vis ? p : 0.0f;
-          }
-          pf[r >> 3][r & 7] = (__bf16)p;
-          dsf[r >> 3][r & 7] = (__bf16)(p * dp[r]);
-        }
-      }
-      // dV^T += dO^T P, dK^T += Q'^T dS
-#pragma unroll
-      for (int db = 0; db < st::kDB; ++db) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<st::kTr>(otr, db, rb, tt),
-                                                              pf[tt], dvacc[db], 0, 0, 0);
-          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<st::kTr>(qtr, db, rb, tt),
-                                                              dsf[tt], dkacc[db], 0, 0, 0);
-        }
-      }
+    }
+  };
+  // One wave per SIMD runs this, so its own instruction order decides how
+  // much hides under the matrix cores: the S / dP products of block 1 are
+  // issued ahead of the softmax of block 0, and the dV / dK products of
+  // block 0 ahead of the softmax of block 1.
+  auto tile = [&](auto masked, int q0, const lchar *set) {
+    f32x16 s0, d0, s1, d1;
+    bf16x8 p0[2], g0[2], p1[2], g1[2];
+    sdp(set, 0, s0, d0);
+    __builtin_amdgcn_sched_barrier(0);
+    sdp(set, 1, s1, d1);
+    softmax(masked, set, q0, 0, s0, d0, p0, g0);
+    __builtin_amdgcn_sched_barrier(0);
+    dkdv(set, 0, p0, g0);
+    softmax(masked, set, q0, 1, s1, d1, p1, g1);
+    __builtin_amdgcn_sched_barrier(0);
+    dkdv(set, 1, p1, g1);
+  };
+  auto compute = [&](int s, const lchar *set) {
+    const int q0 = (qlo + s % per_head) * kBN;  // first query row of the tile
+    const bool need_mask = (prm.causal && q0 < kw0 + 31) ||
+                           (prm.window > 0 && q0 + kBN - 1 >= kw0 + prm.window) ||
+                           (q0 + kBN > N) || (kw0 + 31 >= N);
+    if (need_mask) {
+      tile(std::true_type{}, q0, set);
+    } else {
+      tile(std::false_type{}, q0, set);
     }
   };
 
@@ -422,7 +477,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkdv_kernel(BwdParams prm
   }
 
   if (key < N) {
-    store_rows<D>(prm.dk + kv_slice * D, key, hh, dkacc, prm.ascale);
+    store_rows<D>(prm.dk + kv_slice * D, key, hh, dkacc, prm.scale);
     store_rows<D>(prm.dv + kv_slice * D, key, hh, dvacc, 1.0f);
   }
 }
@@ -443,11 +498,8 @@ BwdParams make_params(const BwdProblem &p) {
   prm.B = p.B; prm.Hq = p.Hq; prm.Hkv = p.Hkv; prm.N = p.N;
   prm.G = p.Hq / p.Hkv;
   prm.nkt = (p.N + kBN - 1) / kBN;
-  const float c = std::fabs(p.scale) * kLog2e;
-  prm.c = c < FLT_MIN ? FLT_MIN : c;
+  prm.c = p.scale * kLog2e;
   prm.scale = p.scale;
-  prm.ascale = std::fabs(p.scale);
-  prm.neg = p.scale < 0.0f ? 1 : 0;
   prm.causal = p.causal;
   prm.window = p.window;
   return prm;

@@ -66,6 +66,15 @@ __device__ __forceinline__ float wave_sum_pair(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
+// Waits here for the load that produced x.  A value loaded before a loop
+// and first read inside it otherwise makes the compiler wait for every
+// outstanding load at that read on each iteration, including the loads of
+// the next tile issued just before.
+template <class T>
+__device__ __forceinline__ void settle(const T &x) {
+  asm volatile("" ::"v"(x));
+}
+
 // Per-lane byte offset of a b128 MFMA fragment in a tile of stride STRIDE:
 // row lane % 32, d = 16 * kk + 8 * (lane / 32) .. + 7 for k-step kk (the
 // k-step's 32 bytes are added by b128_frag).

@@ -64,6 +64,12 @@ def flops(w: Workload) -> int:
     return 4 * w.d * visible_scores(w)
 
 
+def bwd_flops(w: Workload) -> int:
+    """Backward: five 2*d contractions per unmasked score (recomputed S = QK^T,
+    dP = dO V^T, dV += P^T dO, dQ += dS K, dK += dS^T Q)."""
+    return 10 * w.d * visible_scores(w)
+
+
 def algorithmic_bytes(w: Workload) -> int:
     """Q, K, V read once, O (bf16) and lse (fp32) written once."""
     return 2 * w.B * w.N * w.d * (2 * w.Hq + 2 * w.Hkv) + 4 * w.B * w.Hq * w.N
