@@ -18,6 +18,11 @@ Contents
                by the chain rule; pinned by central finite differences of the
                forward oracle, by float64 autograd through masked SDPA and by
                closed forms.
+``decode``     NumPy float64 decode attention over a paged KV cache (gather
+               through the page table, then the plain definition), and the
+               rule that merges results over disjoint key sets; pinned by the
+               forward oracle on the equivalent contiguous cache, by the
+               brute force and by page-permutation and sharing invariants.
 
 What the oracle computes (the plain definition; every page agrees that the
 tiled method returns exactly this result):
@@ -51,4 +56,5 @@ from .attention import (  # noqa: F401
     visible_span,
 )
 from .backward import attention_backward  # noqa: F401
+from .decode import decode_paged, gather_pages, merge_partials  # noqa: F401
 from .brute import brute_attention  # noqa: F401
