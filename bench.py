@@ -9,9 +9,11 @@ already resident in HBM.  Throughput counts 4*d FLOPs per unmasked score
 "The quadratic wall, stated concretely"), never the masked entries a tile
 computes and discards.  Prints one JSON line.
 
-The same line also carries the backward (attn_bwd: dQ, dK, dV) timed on the
-same workload, at 10*d FLOPs per unmasked score (S, dP, dV, dQ, dK: five
-2*d contractions), as a secondary figure.
+The same line also carries, as secondary figures, the backward (attn_bwd:
+dQ, dK, dV) timed on the same workload, at 10*d FLOPs per unmasked score
+(S, dP, dV, dQ, dK: five 2*d contractions), and the paged decode
+(attn_decode_paged) on the decode workloads in HBM GB/s (the visible K and V
+rows once, q, o, lse and the page-table entries).
 """
 
 from __future__ import annotations
@@ -32,6 +34,7 @@ MAIN = "c2_causal_mha"
 OTHERS = ["c2_causal_mha_sharp", "c3_causal_window", "c4_causal_gqa", "c5_long_causal",
           "c5_long_window"]
 BWD_OTHERS = ["c4_causal_gqa"]
+DECODE = ["d1_decode_gqa_128k", "d2_decode_mha_8k", "d3_decode_window_spec4"]
 KERNEL_SRC = os.path.join(ROOT, "exact_tiled_attention_attn_amd", "csrc", "attn_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -137,6 +140,50 @@ def time_backward(w, steps, warmup, torch, attn):
     return ev_ms
 
 
+def time_decode(w, steps, warmup, torch, attn):
+    """attn_decode_paged on a decode workload.  Returns (event ms per call,
+    the sequence lengths)."""
+    from exact_tiled_attention_attn_amd.inputs import decode_lengths, make_decode_q, make_paged_kv
+    lens = decode_lengths(w.B, w.max_len, w.seed)
+    kc, vc, table = make_paged_kv(lens, w.Hkv, w.d, w.page_size, seed=w.seed)
+    dev = torch.device("cuda:0")
+    kc, vc, table = kc.to(dev), vc.to(dev), table.to(dev)
+    q = make_decode_q(w.B, w.Hq, w.T, w.d, seed=w.seed + 1).to(dev)
+    lt = torch.tensor(lens, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.T), dtype=torch.float32, device=dev)
+    nws = attn.attn_decode_workspace_size(w.B, w.Hq, w.Hkv, w.T, w.d, w.page_size, w.max_len,
+                                          w.window)
+    ws = torch.empty((max(nws, 16) // 4,), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        st = attn.attn_decode_paged(q, kc, vc, table, lt, o, lse, ws, w.B, w.Hq, w.Hkv, w.T, w.d,
+                                    w.page_size, kc.shape[0], table.shape[1], w.max_len,
+                                    w.sm_scale, w.window, stream)
+        if st != 0:
+            raise RuntimeError(f"attn_decode_paged: {attn.attn_status_string(st)}")
+
+    t_end = time.perf_counter() + 0.3
+    n = 0
+    while n < warmup or time.perf_counter() < t_end:
+        launch()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ev_ms = e0.elapsed_time(e1) / steps
+    del q, kc, vc, table, lt, o, lse, ws
+    return ev_ms, lens
+
+
 def cpu_baseline(w, host, seconds):
     """The float64 oracle on the host cores, on the same workload: the whole
     workload when it fits in about 2 * `seconds`, else a seeded sample of
@@ -238,6 +285,7 @@ def main():
     ap.add_argument("--no-others", action="store_true", help="time only the main workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-decode", action="store_true", help="skip the paged-decode timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
@@ -251,8 +299,10 @@ def main():
     import torch
 
     from exact_tiled_attention_attn_amd import attn
-    from exact_tiled_attention_attn_amd.workloads import (MI355X_BF16_DENSE_TFLOPS, WORKLOADS,
-                                                          algorithmic_bytes, bwd_flops, flops)
+    from exact_tiled_attention_attn_amd.workloads import (DECODE_WORKLOADS, MI355X_BF16_DENSE_TFLOPS,
+                                                          MI355X_HBM_GBPS, WORKLOADS,
+                                                          algorithmic_bytes, bwd_flops,
+                                                          decode_bytes, flops)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
@@ -336,6 +386,18 @@ def main():
                         "ms": round(em, 4), "flops_per_call": bf}
             torch.cuda.empty_cache()
         out["backward"] = bw
+    if not args.no_decode:
+        dec = {}
+        for name in DECODE if not args.no_others else DECODE[:1]:
+            dw = DECODE_WORKLOADS[name]
+            log(f"timing decode {name}")
+            em, lens = time_decode(dw, args.steps, max(1, args.warmup // 2), torch, attn)
+            nb = decode_bytes(dw, lens)
+            dec[name] = {"GB/s": round(nb / (em * 1e-3) / 1e9, 1),
+                         "frac_of_hbm_peak": round(nb / (em * 1e-3) / 1e9 / MI355X_HBM_GBPS, 4),
+                         "ms": round(em, 4), "bytes_per_call": nb, "seq_lens": lens}
+            torch.cuda.empty_cache()
+        out["decode"] = dec
     if not args.no_cpu:
         log(f"oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)

@@ -1,5 +1,5 @@
-"""MI355X-native exact tiled attention, forward and backward (bf16, causal /
-window / GQA).
+"""MI355X-native exact tiled attention: forward, backward and paged decode
+(bf16, causal / window / GQA).
 
 The compute path is the HIP library ``libattn.so`` built from ``csrc/`` and
 loaded by :mod:`exact_tiled_attention_attn_amd.attn`.  Importing this package
@@ -8,7 +8,8 @@ loudly if the library has not been built.
 """
 
 __all__ = ["attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_bwd_workspace_size",
-           "attn_status_string", "fwd", "bwd", "AttnError"]
+           "attn_decode_paged", "attn_decode_workspace_size", "attn_status_string", "fwd",
+           "bwd", "decode", "AttnError"]
 
 
 def __getattr__(name):

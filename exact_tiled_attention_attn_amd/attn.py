@@ -22,7 +22,8 @@ ATTN_ERR_LAUNCH = 3
 ATTN_MAX_N = 1 << 22
 
 EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_bwd_workspace_size",
-            "attn_num_variants", "attn_variant_name", "attn_status_string", "attn_abi_version")
+            "attn_decode_paged", "attn_decode_workspace_size", "attn_num_variants",
+            "attn_variant_name", "attn_status_string", "attn_abi_version")
 
 
 class AttnError(RuntimeError):
@@ -54,6 +55,10 @@ def load_library():
     lib.attn_bwd.restype = i
     lib.attn_bwd_workspace_size.argtypes = [i, i, i]
     lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.attn_decode_paged.argtypes = [vp] * 8 + [i] * 9 + [f, i, vp]
+    lib.attn_decode_paged.restype = i
+    lib.attn_decode_workspace_size.argtypes = [i] * 8
+    lib.attn_decode_workspace_size.restype = ctypes.c_size_t
     lib.attn_num_variants.argtypes = []
     lib.attn_num_variants.restype = i
     lib.attn_variant_name.argtypes = [i]
@@ -122,6 +127,24 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, sca
 
 def attn_bwd_workspace_size(B, Hq, N):
     return int(load_library().attn_bwd_workspace_size(int(B), int(Hq), int(N)))
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, workspace, B, Hq, Hkv,
+                      T, d, page_size, num_pages, max_pages_per_seq, max_seq_len, scale, window,
+                      stream=None):
+    """Call the C paged-decode entry point; returns its status code."""
+    lib = load_library()
+    return lib.attn_decode_paged(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(o),
+        _ptr(lse), _ptr(workspace), int(B), int(Hq), int(Hkv), int(T), int(d), int(page_size),
+        int(num_pages), int(max_pages_per_seq), int(max_seq_len), float(scale), int(window),
+        _stream(stream, q, k_cache, v_cache, o, lse))
+
+
+def attn_decode_workspace_size(B, Hq, Hkv, T, d, page_size, max_seq_len, window=0):
+    return int(load_library().attn_decode_workspace_size(int(B), int(Hq), int(Hkv), int(T),
+                                                         int(d), int(page_size),
+                                                         int(max_seq_len), int(window)))
 
 
 def attn_num_variants():
@@ -213,3 +236,50 @@ def bwd(q, k, v, o, lse, dout, causal=False, window=0, scale=None, out=None, wor
     if st != ATTN_OK:
         raise AttnError(f"attn_bwd failed: {attn_status_string(st)} (status {st})", st)
     return dq, dk, dv
+
+
+def decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, window=0, scale=None,
+           out=None, workspace=None, stream=None):
+    """Paged decode: allocate (o, lse) and the workspace with torch; raises on
+    any error.
+
+    q: (B, Hq, T, d) bf16; k_cache, v_cache: (num_pages, page_size, Hkv, d)
+    bf16; block_table: (B, max_pages) int32; seq_lens: (B,) int32 (device).
+    Returns o (B, Hq, T, d) bf16 and lse (B, Hq, T) fp32.
+    """
+    import torch
+    for name, t, dt in (("q", q, torch.bfloat16), ("k_cache", k_cache, torch.bfloat16),
+                        ("v_cache", v_cache, torch.bfloat16),
+                        ("block_table", block_table, torch.int32),
+                        ("seq_lens", seq_lens, torch.int32)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise AttnError(f"{name} must be a CUDA (HIP) tensor")
+        if t.dtype != dt:
+            raise AttnError(f"{name} must be {dt}")
+        if not t.is_contiguous():
+            raise AttnError(f"{name} must be contiguous")
+    if q.dim() != 4 or k_cache.dim() != 4 or block_table.dim() != 2 or seq_lens.dim() != 1:
+        raise AttnError("q (B, Hq, T, d), caches (pages, page_size, Hkv, d), "
+                        "block_table (B, max_pages), seq_lens (B,)")
+    B, Hq, T, d = q.shape
+    num_pages, page_size, Hkv, dk = k_cache.shape
+    if (tuple(v_cache.shape) != tuple(k_cache.shape) or dk != d or block_table.shape[0] != B
+            or seq_lens.shape[0] != B):
+        raise AttnError("shapes do not match")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    if workspace is None:
+        nbytes = attn_decode_workspace_size(B, Hq, Hkv, T, d, page_size, max_seq_len,
+                                            max(int(window), 0))
+        workspace = torch.empty((max(nbytes, 16) // 4,), dtype=torch.float32, device=q.device)
+    st = attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, workspace, B, Hq,
+                           Hkv, T, d, page_size, num_pages, block_table.shape[1], max_seq_len,
+                           scale, int(window), stream)
+    if st != ATTN_OK:
+        raise AttnError(f"attn_decode_paged failed: {attn_status_string(st)} (status {st})", st)
+    return o, lse

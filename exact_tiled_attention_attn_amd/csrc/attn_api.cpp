@@ -53,6 +53,30 @@ attn_status_t validate_bwd(const attn::BwdProblem &p) {
   return ATTN_OK;
 }
 
+bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
+
+attn_status_t validate_decode(const attn::DecodeProblem &p) {
+  if (p.B < 0 || p.T < 1 || p.num_pages < 0 || p.max_pages < 0 || p.max_seq_len < 0)
+    return ATTN_ERR_INVALID_ARG;
+  if (p.Hq < 1 || p.Hkv < 1 || p.Hq % p.Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(p.scale)) return ATTN_ERR_INVALID_ARG;
+  if (p.d != 64 && p.d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!pow2_in(p.page_size, 16, 4096)) return ATTN_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(p.Hq / p.Hkv) * p.T > 32) return ATTN_ERR_UNSUPPORTED;
+  if (p.max_seq_len > ATTN_MAX_N) return ATTN_ERR_UNSUPPORTED;
+  if (p.B == 0 || p.max_seq_len == 0) return ATTN_OK;  // nothing to read or write
+  if (!p.q || !p.k_cache || !p.v_cache || !p.block_table || !p.seq_lens || !p.o || !p.lse ||
+      !p.workspace)
+    return ATTN_ERR_INVALID_ARG;
+  if (p.num_pages < 1 || p.max_pages < 1) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(p.q) || !aligned16(p.k_cache) || !aligned16(p.v_cache) || !aligned16(p.o) ||
+      !aligned16(p.lse) || !aligned16(p.workspace) ||
+      (reinterpret_cast<uintptr_t>(p.block_table) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(p.seq_lens) & 3u) != 0)
+    return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -95,6 +119,34 @@ attn_status_t attn_bwd(const void *q, const void *k, const void *v, const void *
   if (p.window >= N) p.window = 0;
   if (p.window < 0) p.window = 0;
   const hipError_t e = attn::launch_bwd(p, static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidValue) return ATTN_ERR_UNSUPPORTED;
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int T, int d, int page_size,
+                                  int max_seq_len, int window) {
+  if (Hkv < 1 || Hq < 1 || Hq % Hkv != 0 || (d != 64 && d != 128)) return 0;
+  const attn::DecodePlan plan =
+      attn::plan_decode(B, Hq, Hkv, T, d, page_size, max_seq_len, window);
+  return (plan.part_o_floats + plan.part_lse_floats) * sizeof(float);
+}
+
+attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
+                                const int *block_table, const int *seq_lens, void *o, float *lse,
+                                void *workspace, int B, int Hq, int Hkv, int T, int d,
+                                int page_size, int num_pages, int max_pages_per_seq,
+                                int max_seq_len, float scale, int window, void *stream) {
+  attn::DecodeProblem p{q,  k_cache, v_cache, block_table, seq_lens,          o,
+                        lse, workspace, B,      Hq,          Hkv,               T,
+                        d,  page_size, num_pages, max_pages_per_seq, max_seq_len, scale,
+                        window};
+  const attn_status_t st = validate_decode(p);
+  if (st != ATTN_OK) return st;
+  if (B == 0 || max_seq_len == 0) return ATTN_OK;
+  if (p.window < 0) p.window = 0;
+  const attn::DecodePlan plan =
+      attn::plan_decode(B, Hq, Hkv, T, d, page_size, max_seq_len, p.window);
+  const hipError_t e = attn::launch_decode(p, plan, static_cast<hipStream_t>(stream));
   if (e == hipErrorInvalidValue) return ATTN_ERR_UNSUPPORTED;
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }

@@ -1,0 +1,408 @@
+// gfx950 (MI355X, CDNA4) decode attention over a paged KV cache, split over
+// the keys.
+//
+// What is computed: "Efficient attention: long context and sub-quadratic
+// variants", section "FlashAttention: exact attention, IO-aware", describes
+// PagedAttention: the KV cache sits in fixed-size pages, each sequence has a
+// page table, attention gathers K and V through it, and the result is the
+// exact attention.  The T newest tokens of sequence b are the queries; query
+// t sits at position L_b - T + t and sees the cached keys j <= that position
+// (and j > pos - window with a window); query head h reads KV head
+// h / (Hq / Hkv).
+//
+// Schedule (split-KV): one single-wave workgroup per (sequence, KV head,
+// key range of `chunk` keys).  The G query heads x T tokens of the KV group
+// are the wave's (at most 32) MFMA columns, so every cached K/V byte is read
+// from HBM once for all the heads that share it.  32-key tiles are gathered
+// through the page table (two 16-row groups per tile, each inside one page)
+// and staged two tiles ahead through registers into the wave's LDS tile.
+// Per tile: S^T = K Q^T (8 MFMA), running max / sum per column, O^T += V^T
+// P^T (8 MFMA, V^T by transposing LDS reads).  The split writes its
+// normalised partial (O_s, lse_s); attn_decode_merge_kernel combines the
+// splits with lse = ln sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s,
+// which is the running softmax's rescaling applied once per split.
+//
+// The kernel is bound by HBM: per cached token it reads 2 x d x 2 bytes and
+// does 4 d G T FLOPs.
+
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <cmath>
+#include <cstdint>
+
+#include "attn_device.h"
+#include "attn_internal.h"
+
+namespace attn {
+namespace {
+
+using namespace dev;
+
+constexpr int kKeys = 32;       // keys per tile
+constexpr int kMaxEntries = 64;  // page-table entries per split (one per lane)
+
+struct DecParams {
+  const uint16_t *q, *kc, *vc;  // q [B][Hq][T][D]; caches [pages][PS][Hkv][D]
+  const int *table, *lens;      // [B][max_pages], [B]
+  uint16_t *o;                  // [B][Hq][T][D]
+  float *lse;                   // [B][Hq][T]
+  float *part_o;                // [B][Hkv][nsplit][ncols][D]
+  float *part_lse;              // [B][Hkv][nsplit][ncols]
+  int B, Hq, Hkv, G, T, ncols;  // ncols = G * T <= 32
+  int ps, ps_shift;             // page size (power of two)
+  int num_pages, max_pages;
+  int nsplit, chunk;            // keys per split: multiple of unit
+  int unit;                     // max(32, ps): splits start on a page and a tile
+  float c;                      // |scale| * log2(e), at least FLT_MIN
+  int neg;                      // scale < 0: q is negated on load
+  int window;                   // 0: none
+};
+
+template <int D>
+struct DecTile {
+  using st = Stride<D>;
+  static constexpr int kKB = kKeys * st::kB128;  // K tile, b128 stride
+  static constexpr int kVB = kKeys * st::kTr;    // V tile, transposed-read stride
+  static constexpr int kSet = kKB + kVB;
+  static constexpr int kLoads = kKeys * st::kCh / 64;  // b128 per lane per tensor
+  static constexpr int kRowsPerLoad = 64 / st::kCh;
+};
+
+// Buffer descriptor over the 16 cached rows starting at token j (a multiple
+// of 16, so the rows lie in one page) of KV head kvh; rows at or past the
+// sequence length, and every row of an out-of-range page index, read as 0.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t group_rsrc(const uint16_t *cache,
+                                                           const DecParams &prm, int page,
+                                                           int j, int L, int kvh) {
+  const int valid = min(max(L - j, 0), 16);
+  const bool ok = valid > 0 && page >= 0 && page < prm.num_pages;
+  const size_t row = (size_t)page * prm.ps + (j & (prm.ps - 1));
+  const uint16_t *base = cache + (ok ? (row * prm.Hkv + kvh) * D : 0);
+  const uint32_t stride = (uint32_t)prm.Hkv * D * 2;
+  const uint32_t bytes = ok ? (uint32_t)(valid - 1) * stride + D * 2 : 0;
+  return make_rsrc(base, bytes);
+}
+
+template <int D>
+struct DecStage {
+  using tl = DecTile<D>;
+  u32x4 k[tl::kLoads], v[tl::kLoads];
+
+  // Tile of keys j0 .. j0 + 31; lane loads row 4n + lane / 16 (n-th load),
+  // 16-byte chunk lane % 16 of it (for D = 128).
+  __device__ __forceinline__ void load(const DecParams &prm, int page0, int page1, int j0, int L,
+                                       int kvh, int lane) {
+    const __amdgpu_buffer_rsrc_t k0 = group_rsrc<D>(prm.kc, prm, page0, j0, L, kvh);
+    const __amdgpu_buffer_rsrc_t k1 = group_rsrc<D>(prm.kc, prm, page1, j0 + 16, L, kvh);
+    const __amdgpu_buffer_rsrc_t v0 = group_rsrc<D>(prm.vc, prm, page0, j0, L, kvh);
+    const __amdgpu_buffer_rsrc_t v1 = group_rsrc<D>(prm.vc, prm, page1, j0 + 16, L, kvh);
+    const uint32_t stride = (uint32_t)prm.Hkv * D * 2;
+    const int r_lane = lane / Stride<D>::kCh, ch = lane % Stride<D>::kCh;
+#pragma unroll
+    for (int n = 0; n < tl::kLoads; ++n) {
+      const int r = n * tl::kRowsPerLoad + r_lane;  // tile row 0 .. 31
+      const uint32_t off = (uint32_t)(r & 15) * stride + ch * 16;
+      const bool hi = n * tl::kRowsPerLoad >= 16;   // compile-time per n
+      k[n] = __builtin_amdgcn_raw_buffer_load_b128(hi ? k1 : k0, off, 0, 0);
+      v[n] = __builtin_amdgcn_raw_buffer_load_b128(hi ? v1 : v0, off, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(lchar *set, int lane) const {
+    const int r_lane = lane / Stride<D>::kCh, ch = lane % Stride<D>::kCh;
+#pragma unroll
+    for (int n = 0; n < tl::kLoads; ++n) {
+      const int r = n * tl::kRowsPerLoad + r_lane;
+      *(lds_u32x4_t *)(set + r * Stride<D>::kB128 + ch * 16) = k[n];
+      *(lds_u32x4_t *)(set + tl::kKB + r * Stride<D>::kTr + ch * 16) = v[n];
+    }
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(64) void attn_decode_split_kernel(DecParams prm) {
+  using st = Stride<D>;
+  using tl = DecTile<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[tl::kSet];
+
+  const int lane = threadIdx.x;
+  const int l32 = lane & 31, hh = lane >> 5;
+  // blockIdx.x = (b * nsplit + split) * Hkv + kvh: the Hkv workgroups that
+  // read the same cache pages (token rows hold every KV head) run together,
+  // so each page is streamed from HBM in one pass rather than in Hkv
+  // scattered 256-byte pieces
+  const int kvh = blockIdx.x % prm.Hkv;
+  const int bs = blockIdx.x / prm.Hkv;
+  const int split = bs % prm.nsplit, b = bs / prm.nsplit;
+  const int bk = b * prm.Hkv + kvh;
+  const int L = prm.lens[b];
+  const int T = prm.T;
+
+  // this lane's column: query head kvh * G + g, token t
+  const int col = l32;
+  const bool col_ok = col < prm.ncols;
+  const int g = col_ok ? col / T : 0, t = col_ok ? col % T : 0;
+  const int pos = L - T + t;                   // position of the query token
+  const int m_lo = prm.window > 0 ? max(0, pos - prm.window + 1) : 0;
+  const int m_span = col_ok && pos >= 0 ? pos - m_lo + 1 : 0;  // visible keys [m_lo, pos]
+
+  // key range of this split: the splits tile the keys any column sees,
+  // from the window start of the first query (rounded down to a page and a
+  // tile) on
+  const int lo_all = prm.window > 0 ? max(0, L - T - prm.window + 1) : 0;
+  const int s_lo = (lo_all / prm.unit) * prm.unit + split * prm.chunk;
+  const int k_begin = max(s_lo, lo_all & ~(kKeys - 1));
+  const int k_end = min(s_lo + prm.chunk, L);
+  const int ntiles = k_end > k_begin ? (k_end - k_begin + kKeys - 1) / kKeys : 0;
+
+  // page-table entries of the split: lane i holds entry s_lo / ps + i
+  const int e0 = s_lo >> prm.ps_shift;
+  int entry = -1;
+  if (e0 + lane < prm.max_pages && lane < kMaxEntries)
+    entry = prm.table[(size_t)b * prm.max_pages + e0 + lane];
+  auto page_of = [&](int j) {  // page holding token j of this split
+    return __builtin_amdgcn_readlane(entry, (j >> prm.ps_shift) - e0);
+  };
+
+  // Q^T operand: column col, d = 16 kk + 8 hh ..
+  const size_t q_row = ((size_t)(b * prm.Hq + kvh * prm.G + g) * T + t);
+  bf16x8 qf[st::kKSteps];
+#pragma unroll
+  for (int kk = 0; kk < st::kKSteps; ++kk) {
+    qf[kk] = row_frag<D>(prm.q + q_row * D, 0, col_ok ? 1 : 0, 16 * kk + 8 * hh, prm.neg);
+    settle(qf[kk]);
+  }
+  settle(entry);
+
+  f32x16 oacc[st::kDB];
+#pragma unroll
+  for (int i = 0; i < st::kDB; ++i) oacc[i] = f32x16{};
+  float m2 = -1e30f, lsum = 0.0f, lrnd = 0.0f;
+  const float c = prm.c;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  const int kb_lane = b128_lane_off<st::kB128>(lane);
+  const int vt_lane = tr_lane_off<st::kTr>(lane);
+
+  auto compute = [&](int j0, const lchar *set) {
+    // S^T: register r holds key j0 + 8 (r / 4) + 4 hh + r % 4 of this column
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < st::kKSteps; ++kk)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b128_frag<st::kB128>(set + kb_lane, kk, 0),
+                                                  qf[kk], s, 0, 0, 0);
+    // every valid column sees the whole tile when it starts at or after the
+    // last column's window start and ends at or before the first column's
+    // position
+    const bool need_mask = (prm.window > 0 && j0 < L - prm.window) || j0 + kKeys - 1 > L - T;
+    if (need_mask) {
+      const int base = j0 + 4 * hh - m_lo;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        s[r] = (unsigned)(base + 8 * (r >> 2) + (r & 3)) < (unsigned)m_span ? s[r] : -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = wave_max_pair(mx) * c;  // scaled, log2 units; -inf if nothing visible
+    const float mnew = fmaxf(m2, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+    m2 = mnew;
+    bf16x8 pf[2];
+    float ps = 0.0f, pr = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -mnew));
+      ps += p;
+      pf[r >> 3][r & 7] = (__bf16)p;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bf16x2 pair = {pf[i >> 2][2 * (i & 3)], pf[i >> 2][2 * (i & 3) + 1]};
+      pr = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, pr, false);
+    }
+    lsum = lsum * alpha + wave_sum_pair(ps);
+    lrnd = lrnd * alpha + wave_sum_pair(pr);
+#pragma unroll
+    for (int db = 0; db < st::kDB; ++db) {
+      oacc[db] *= alpha;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tr_frag<st::kTr>(set + tl::kKB + vt_lane, db, 0, tt), pf[tt], oacc[db], 0, 0, 0);
+    }
+  };
+
+  // One LDS tile per wave: the wave's LDS instructions execute in order,
+  // so the next tile's stores, issued after this tile's reads, cannot
+  // overwrite data those reads still have to return.  Two tiles are in
+  // flight in registers (sa, sb) while one is computed.
+  lchar *const set = (lchar *)smem;
+  DecStage<D> sa, sb;
+  auto tile_j0 = [&](int i) { return k_begin + i * kKeys; };
+  auto issue = [&](DecStage<D> &sg, int i) {
+    const int j0 = tile_j0(i);
+    sg.load(prm, page_of(j0), page_of(j0 + 16), j0, L, kvh, lane);
+  };
+  if (ntiles > 0) issue(sa, 0);
+  if (ntiles > 1) issue(sb, 1);
+  if (ntiles > 0) sa.store(set, lane);
+  for (int i = 0; i < ntiles; i += 2) {
+    // tile i is in LDS, tile i + 1 in sb; tile i + 2 loads into sa
+    if (i + 2 < ntiles) issue(sa, i + 2);
+    compute(tile_j0(i), set);
+    if (i + 1 >= ntiles) break;
+    sb.store(set, lane);
+    if (i + 3 < ntiles) issue(sb, i + 3);
+    compute(tile_j0(i + 1), set);
+    if (i + 2 < ntiles) sa.store(set, lane);
+  }
+
+  // partial result of this split for the lane's column
+  const bool any = lsum > 0.0f;
+  const float lse_s = any ? (m2 + __log2f(lsum)) * kLn2 : -INFINITY;
+  const float inv = any ? 1.0f / lrnd : 0.0f;
+  if (col_ok) {
+    const size_t slot = ((size_t)bk * prm.nsplit + split) * prm.ncols + col;
+    float *po = prm.part_o + slot * D + 4 * hh;
+#pragma unroll
+    for (int db = 0; db < st::kDB; ++db) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = oacc[db][4 * i + j] * inv;
+        *(f32x4 *)(po + 32 * db + 8 * i) = w;
+      }
+    }
+    if (hh == 0) prm.part_lse[slot] = lse_s;
+  }
+}
+
+// Merges the splits of one (sequence, KV head, column): one wave; the
+// lanes first reduce the splits' lse maximum, then each lane accumulates
+// D / 64 values of O over the splits.  Only splits of a sequence that holds
+// keys matter; the others have lse = -inf.
+template <int D>
+__global__ __launch_bounds__(64) void attn_decode_merge_kernel(DecParams prm) {
+  constexpr int kPer = D / 64;  // d values per lane
+  const int lane = threadIdx.x;
+  const int col = blockIdx.x % prm.ncols;
+  const int bk = blockIdx.x / prm.ncols;
+  const int b = bk / prm.Hkv, kvh = bk % prm.Hkv;
+  const size_t slot0 = (size_t)bk * prm.nsplit * prm.ncols + col;
+  float m = -INFINITY;
+  for (int s = lane; s < prm.nsplit; s += 64)
+    m = fmaxf(m, prm.part_lse[slot0 + (size_t)s * prm.ncols]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  // every split wrote its slot (an empty one o = 0, lse = -inf, whose weight
+  // exp(-inf - m) is 0), so the walk is branch-free; eight splits per step
+  // keep eight loads in flight per lane
+  float acc[kPer] = {};
+  float tot = 0.0f;
+  if (m > -INFINITY) {
+    constexpr int kU = 8;
+    for (int s0 = 0; s0 < prm.nsplit; s0 += kU) {
+      float ls[kU], ov[kU][kPer];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const bool in = s0 + u < prm.nsplit;
+        const size_t slot = slot0 + (size_t)(in ? s0 + u : 0) * prm.ncols;
+        ls[u] = in ? prm.part_lse[slot] : -INFINITY;
+        const float *po = prm.part_o + slot * D + lane * kPer;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) ov[u][j] = po[j];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const float w = __expf(ls[u] - m);
+        tot += w;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) acc[j] += w * ov[u][j];
+      }
+    }
+  }
+  const int g = col / prm.T, t = col % prm.T;
+  const size_t row = (size_t)(b * prm.Hq + kvh * prm.G + g) * prm.T + t;
+  const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const __bf16 x = (__bf16)(acc[j] * inv);
+    prm.o[row * D + lane * kPer + j] = __builtin_bit_cast(uint16_t, x);
+  }
+  if (lane == 0) prm.lse[row] = tot > 0.0f ? m + __logf(tot) : -INFINITY;
+}
+
+template <int D>
+hipError_t launch_decode_d(const DecodeProblem &p, const DecodePlan &plan, hipStream_t stream) {
+  DecParams prm;
+  prm.q = static_cast<const uint16_t *>(p.q);
+  prm.kc = static_cast<const uint16_t *>(p.k_cache);
+  prm.vc = static_cast<const uint16_t *>(p.v_cache);
+  prm.table = p.block_table;
+  prm.lens = p.seq_lens;
+  prm.o = static_cast<uint16_t *>(p.o);
+  prm.lse = p.lse;
+  prm.part_o = static_cast<float *>(p.workspace);
+  prm.part_lse = prm.part_o + plan.part_o_floats;
+  prm.B = p.B; prm.Hq = p.Hq; prm.Hkv = p.Hkv; prm.G = p.Hq / p.Hkv; prm.T = p.T;
+  prm.ncols = prm.G * p.T;
+  prm.ps = p.page_size;
+  prm.ps_shift = __builtin_ctz((unsigned)p.page_size);
+  prm.num_pages = p.num_pages;
+  prm.max_pages = p.max_pages;
+  prm.nsplit = plan.nsplit;
+  prm.chunk = plan.chunk;
+  prm.unit = p.page_size > kKeys ? p.page_size : kKeys;
+  const float c = std::fabs(p.scale) * kLog2e;
+  prm.c = c < FLT_MIN ? FLT_MIN : c;
+  prm.neg = p.scale < 0.0f ? 1 : 0;
+  prm.window = p.window;
+  const long long groups = (long long)p.B * p.Hkv;
+  const long long wgs = groups * plan.nsplit;
+  if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
+  void *args[] = {&prm};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&attn_decode_split_kernel<D>),
+                                 dim3((unsigned)wgs), dim3(64), args, 0, stream);
+  if (e != hipSuccess) return e;
+  const long long merges = groups * prm.ncols;
+  if (merges > 0x7fffffffLL) return hipErrorInvalidValue;
+  return hipLaunchKernel(reinterpret_cast<const void *>(&attn_decode_merge_kernel<D>),
+                         dim3((unsigned)merges), dim3(64), args, 0, stream);
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int B, int Hq, int Hkv, int T, int d, int page_size, int max_seq_len,
+                       int window) {
+  DecodePlan plan{};
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || page_size <= 0 || max_seq_len <= 0) return plan;
+  const int unit = page_size > kKeys ? page_size : kKeys;
+  // keys a sequence's queries can see: all of them, or the last window + T - 1
+  // (plus up to one unit of rounding at the start)
+  long long span = max_seq_len;
+  if (window > 0 && (long long)window + T - 1 + unit < span) span = (long long)window + T - 1 + unit;
+  const long long max_chunk = (long long)kMaxEntries * page_size;  // one table entry per lane
+  // enough single-wave workgroups to keep every CU's four LDS slots busy
+  // several times over: about 8192 in total
+  const long long groups = (long long)B * Hkv;
+  long long want = (8192 + groups - 1) / groups;
+  long long chunk = (span + want - 1) / want;
+  chunk = (chunk + unit - 1) / unit * unit;
+  if (chunk < unit) chunk = unit;
+  if (chunk > max_chunk) chunk = max_chunk;
+  plan.chunk = (int)chunk;
+  plan.nsplit = (int)((span + chunk - 1) / chunk);
+  const long long ncols = (long long)(Hq / Hkv) * T;
+  plan.part_o_floats = (size_t)groups * plan.nsplit * ncols * d;
+  plan.part_lse_floats = (size_t)groups * plan.nsplit * ncols;
+  return plan;
+}
+
+hipError_t launch_decode(const DecodeProblem &p, const DecodePlan &plan, hipStream_t stream) {
+  return p.d == 128 ? launch_decode_d<128>(p, plan, stream) : launch_decode_d<64>(p, plan, stream);
+}
+
+}  // namespace attn

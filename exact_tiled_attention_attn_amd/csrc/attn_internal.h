@@ -1,9 +1,11 @@
 // Private interface between the C ABI entry points (attn_api.cpp) and the
-// gfx950 kernels (attn_fwd.hip, attn_bwd.hip).  Not installed, not part of
-// the ABI.
+// gfx950 kernels (attn_fwd.hip, attn_bwd.hip, attn_decode.hip).  Not
+// installed, not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
+
+#include <cstddef>
 
 namespace attn {
 
@@ -44,5 +46,32 @@ struct BwdProblem {
 
 // Enqueue the three backward kernels (Delta, dQ, dK/dV) for `p` on `stream`.
 hipError_t launch_bwd(const BwdProblem &p, hipStream_t stream);
+
+// One paged decode problem, already validated by the entry point.
+struct DecodeProblem {
+  const void *q, *k_cache, *v_cache;
+  const int *block_table, *seq_lens;
+  void *o;
+  float *lse;
+  void *workspace;
+  int B, Hq, Hkv, T, d, page_size, num_pages, max_pages, max_seq_len;
+  float scale;
+  int window;  // <= 0: none
+};
+
+// How the keys are split: nsplit ranges of `chunk` keys; the workspace
+// holds part_o_floats partial outputs followed by part_lse_floats lse values.
+struct DecodePlan {
+  int nsplit, chunk;
+  size_t part_o_floats, part_lse_floats;
+};
+
+// Deterministic in its arguments: the workspace size query and the launch
+// agree.  All zero for a non-positive argument.
+DecodePlan plan_decode(int B, int Hq, int Hkv, int T, int d, int page_size, int max_seq_len,
+                       int window);
+
+// Enqueue the split kernel and the merge kernel for `p` on `stream`.
+hipError_t launch_decode(const DecodeProblem &p, const DecodePlan &plan, hipStream_t stream);
 
 }  // namespace attn

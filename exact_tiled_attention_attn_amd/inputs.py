@@ -13,6 +13,14 @@ per-slice drawing keeps host memory bounded at the longest shapes.
 
 The upstream gradient dO of the backward is drawn the same way, from its own
 seed, as one (B, Hq, N, d) tensor of N(0, 1) values rounded to bfloat16.
+
+Paged decode inputs: per sequence b, its L_b cached tokens are drawn like K
+and V (one (L_b, Hkv, d) slice each, N(0, 1) rounded to bf16) and written
+into pages of a cache whose physical pages are a seeded random permutation
+(so consecutive pages of a sequence are scattered); pages that no sequence
+uses hold N(0, 1) values too.  The queries (B, Hq, T, d) are drawn the same
+way.  Context lengths for the workloads are seeded uniform integers in
+[1, max_len] (``decode_lengths``).
 """
 
 from __future__ import annotations
@@ -43,6 +51,56 @@ def make_dout(B: int, Hq: int, N: int, d: int, seed: int) -> torch.Tensor:
     """Return a bf16 CPU tensor dO shaped (B, Hq, N, d)."""
     gen = torch.Generator().manual_seed(int(seed))
     return _draw(gen, B, Hq, N, d)
+
+
+def decode_lengths(B: int, max_len: int, seed: int) -> list[int]:
+    """Seeded context lengths, uniform in [1, max_len]."""
+    rng = np.random.default_rng(int(seed))
+    return [int(x) for x in rng.integers(1, max_len + 1, size=B)]
+
+
+def make_paged_kv(lens, Hkv: int, d: int, page_size: int, seed: int, extra_pages: int = 2):
+    """Return (k_cache, v_cache, block_table) as CPU tensors.
+
+    k_cache, v_cache: bf16 (num_pages, page_size, Hkv, d); block_table:
+    int32 (B, max_pages) with max_pages = max ceil(L_b / page_size) (at least
+    1); entries past a sequence's pages are -1.
+    """
+    gen = torch.Generator().manual_seed(int(seed))
+    rng = np.random.default_rng(int(seed) + 1)
+    npg = [(int(L) + page_size - 1) // page_size for L in lens]
+    num_pages = sum(npg) + extra_pages
+    max_pages = max(max(npg), 1)
+    perm = rng.permutation(num_pages)
+    kc = torch.empty((num_pages, page_size, Hkv, d), dtype=torch.bfloat16)
+    vc = torch.empty_like(kc)
+    table = torch.full((len(lens), max_pages), -1, dtype=torch.int32)
+    used = np.zeros(num_pages, dtype=bool)
+    nxt = 0
+    for b, L in enumerate(lens):
+        k = torch.randn((int(L), Hkv, d), generator=gen, dtype=torch.float32).to(torch.bfloat16)
+        v = torch.randn((int(L), Hkv, d), generator=gen, dtype=torch.float32).to(torch.bfloat16)
+        for p in range(npg[b]):
+            page = int(perm[nxt])
+            nxt += 1
+            used[page] = True
+            table[b, p] = page
+            n = min(page_size, int(L) - p * page_size)
+            kc[page, :n] = k[p * page_size:p * page_size + n]
+            vc[page, :n] = v[p * page_size:p * page_size + n]
+            if n < page_size:
+                kc[page, n:] = torch.randn((page_size - n, Hkv, d), generator=gen).to(torch.bfloat16)
+                vc[page, n:] = torch.randn((page_size - n, Hkv, d), generator=gen).to(torch.bfloat16)
+    for page in np.nonzero(~used)[0]:
+        kc[page] = torch.randn((page_size, Hkv, d), generator=gen).to(torch.bfloat16)
+        vc[page] = torch.randn((page_size, Hkv, d), generator=gen).to(torch.bfloat16)
+    return kc, vc, table
+
+
+def make_decode_q(B: int, Hq: int, T: int, d: int, seed: int) -> torch.Tensor:
+    """Return bf16 queries (B, Hq, T, d)."""
+    gen = torch.Generator().manual_seed(int(seed))
+    return _draw(gen, B, Hq, T, d)
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:

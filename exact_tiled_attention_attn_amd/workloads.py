@@ -88,3 +88,53 @@ WORKLOADS = {
     "c5_long_window": Workload("c5_long_window", 1, 32, 32, 131072, 128, True, 4096, 5,
                                sampled_rows=256),
 }
+
+
+# ---------------------------------------------------------------------------
+# Paged decode workloads: the serving-side sibling ("FlashAttention: exact
+# attention, IO-aware", PagedAttention).  Shapes from the same pages: the
+# 64 / 8 GQA heads and d = 128, contexts up to the 128k of "The quadratic
+# wall, stated concretely", the window 4096 of "Sliding-window and local
+# attention"; a batch of sequences with a seeded uniform length mix.
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    T: int
+    d: int
+    page_size: int
+    max_len: int
+    seed: int
+    window: int = 0
+
+    @property
+    def sm_scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+def decode_visible_keys(w: DecodeWorkload, L: int) -> int:
+    """Cached tokens any query of a length-L sequence sees (each is read once)."""
+    if w.window > 0:
+        return min(L, w.window + w.T - 1)
+    return L
+
+
+def decode_bytes(w: DecodeWorkload, lens) -> int:
+    """Algorithmic HBM bytes of one call: the visible K and V rows once, q and o
+    (bf16), lse (fp32), the page-table entries and lengths read."""
+    kv = sum(decode_visible_keys(w, L) for L in lens) * w.Hkv * w.d * 2 * 2
+    qo = 2 * w.B * w.Hq * w.T * w.d * 2 + 4 * w.B * w.Hq * w.T
+    table = sum((L + w.page_size - 1) // w.page_size for L in lens) * 4 + 4 * w.B
+    return kv + qo + table
+
+
+DECODE_WORKLOADS = {
+    "d1_decode_gqa_128k": DecodeWorkload("d1_decode_gqa_128k", 8, 64, 8, 1, 128, 64, 131072, 21),
+    "d2_decode_mha_8k": DecodeWorkload("d2_decode_mha_8k", 32, 32, 32, 1, 128, 16, 8192, 22),
+    "d3_decode_window_spec4": DecodeWorkload("d3_decode_window_spec4", 8, 64, 8, 4, 128, 256,
+                                             131072, 23, window=4096),
+}

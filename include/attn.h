@@ -1,6 +1,6 @@
 /*
  * attn.h -- C ABI of the MI355X (gfx950) exact tiled attention: the forward
- * pass and its gradients.
+ * pass, its gradients, and decode over a paged KV cache.
  *
  * Operation.  For every batch b, query head h and query row i
  *
@@ -139,6 +139,54 @@ attn_status_t attn_bwd(const void *q, const void *k, const void *v, const void *
  * invalid shape).  The library never allocates it itself. */
 size_t attn_bwd_workspace_size(int B, int Hq, int N);
 
+/* Decode over a paged KV cache.  "Efficient attention: long context and
+ * sub-quadratic variants" (section "FlashAttention: exact attention,
+ * IO-aware") describes PagedAttention: the cache is stored in fixed-size
+ * pages with a per-sequence page table, kernels gather K and V through the
+ * table, sequences may share pages, and the result is exact attention.
+ *
+ * For sequence b with L = seq_lens[b] cached tokens, token j is slot
+ * j % page_size of physical page block_table[b * max_pages_per_seq +
+ * j / page_size].  Its T newest tokens are the queries: query t sits at
+ * position pos = L - T + t and sees the cached keys j <= pos, and with
+ * window > 0 only j > pos - window.  Query head h reads KV head
+ * h / (Hq / Hkv).  Per (b, h, t):
+ *     o   = sum_j softmax_j(scale * <q, k_j>) v_j,   lse = ln sum_j exp(...)
+ * over the visible keys; a query that sees no key gets o = 0, lse = -inf.
+ *
+ *   q            bf16 [B][Hq][T][d]
+ *   k_cache,     bf16 [num_pages][page_size][Hkv][d]
+ *   v_cache
+ *   block_table  int32 [B][max_pages_per_seq], physical page indices; an
+ *                index outside [0, num_pages) reads as zero rows
+ *   seq_lens     int32 [B], device memory, each in [0, max_seq_len] and
+ *                covered by the table row (the host never reads it)
+ *   o            bf16 [B][Hq][T][d]   written
+ *   lse          fp32 [B][Hq][T]      written
+ *   workspace    attn_decode_workspace_size(...) bytes of device memory,
+ *                16-byte aligned, contents unspecified on entry and exit
+ *   page_size    a power of two in [16, 4096]
+ *   max_seq_len  host-side upper bound of seq_lens (decides the key split)
+ *   scale        as for attn_fwd; window <= 0: none
+ * Requires (Hq / Hkv) * T <= 32 (the query heads of one KV head times the
+ * new tokens fill one matrix-core column block).  Keys are split into
+ * ranges processed by separate workgroups; the partial results are merged
+ * with lse = ln sum_s exp(lse_s), o = sum_s exp(lse_s - lse) o_s.  Two
+ * kernels are enqueued on `stream`.  Errors as for attn_fwd (also: T < 1,
+ * page size, heads x tokens > 32, unaligned table or lens -> codes as
+ * listed); B == 0 or max_seq_len == 0 launches nothing. */
+attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
+                                const int *block_table, const int *seq_lens, void *o, float *lse,
+                                void *workspace, int B, int Hq, int Hkv, int T, int d,
+                                int page_size, int num_pages, int max_pages_per_seq,
+                                int max_seq_len, float scale, int window, void *stream);
+
+/* Bytes of workspace attn_decode_paged needs for these arguments (0 for an
+ * invalid or empty shape).  A window (> 0) shortens the span of keys the
+ * split covers and so the workspace. */
+size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int T, int d, int page_size,
+                                  int max_seq_len, int window);
+
 /* Number of variant ids accepted by attn_fwd_ex (ids 0 .. n-1). */
 int attn_num_variants(void);
 
@@ -149,7 +197,7 @@ const char *attn_variant_name(int variant);
 const char *attn_status_string(attn_status_t status);
 
 /* ABI version of this header (incremented on any signature change). */
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 int attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -168,3 +168,59 @@ def test_bwd_workspace_size(lib):
     assert attn.attn_bwd_workspace_size(0, 32, 8192) == 0
     assert attn.attn_bwd_workspace_size(1, 1, -3) == 0
     assert attn.attn_bwd_workspace_size(3, 64, 1 << 22) == 3 * 64 * (1 << 22) * 4
+
+
+DEC_GOOD = dict(q=P, k_cache=P, v_cache=P, block_table=P, seq_lens=P, o=P, lse=P, workspace=P,
+                B=2, Hq=8, Hkv=2, T=1, d=128, page_size=16, num_pages=10,
+                max_pages_per_seq=5, max_seq_len=80, scale=0.1, window=0)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(k_cache=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(block_table=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(seq_lens=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(workspace=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(lse=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(B=-1), attn.ATTN_ERR_INVALID_ARG),
+    (dict(T=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_INVALID_ARG),
+    (dict(num_pages=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(max_pages_per_seq=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), attn.ATTN_ERR_INVALID_ARG),
+    (dict(d=96), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(page_size=24), attn.ATTN_ERR_UNSUPPORTED),     # not a power of two
+    (dict(page_size=8), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(page_size=8192), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(T=9), attn.ATTN_ERR_UNSUPPORTED),              # 4 heads x 9 tokens > 32
+    (dict(block_table=P + 2), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(o=P + 8), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(max_seq_len=(1 << 22) + 1), attn.ATTN_ERR_UNSUPPORTED),
+])
+def test_decode_rejects_bad_arguments_without_launching(lib, kw, expect):
+    a = dict(DEC_GOOD)
+    a.update(kw)
+    assert attn.attn_decode_paged(**a) == expect
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(max_seq_len=0),
+                                dict(B=0, q=0, k_cache=0, v_cache=0, block_table=0, seq_lens=0,
+                                     o=0, lse=0, workspace=0)])
+def test_decode_empty_problem_is_ok_and_launches_nothing(lib, kw):
+    a = dict(DEC_GOOD)
+    a.update(kw)
+    assert attn.attn_decode_paged(**a) == attn.ATTN_OK
+
+
+def test_decode_workspace_size(lib):
+    n = attn.attn_decode_workspace_size(8, 64, 8, 1, 128, 64, 131072)
+    assert attn.attn_decode_workspace_size(8, 64, 8, 1, 128, 64, 131072, 4096) < n
+    assert n > 0 and n % 4 == 0
+    # partial outputs (d floats) and lse (1 float) per (sequence, KV head, split, column)
+    per = 8 * 8 * 8 * (128 + 1) * 4
+    assert n % per == 0
+    assert attn.attn_decode_workspace_size(0, 64, 8, 1, 128, 64, 1000) == 0
+    assert attn.attn_decode_workspace_size(2, 64, 7, 1, 128, 64, 1000) == 0
+    # the split never exceeds 64 page-table entries
+    n16 = attn.attn_decode_workspace_size(1, 1, 1, 1, 64, 16, 1 << 20)
+    assert n16 // ((64 + 1) * 4) >= (1 << 20) // (64 * 16)

@@ -1,0 +1,151 @@
+"""GPU parity of paged split-KV decode against the float64 decode oracle.
+
+Bar (the forward's): O max |err| <= 2e-2 and mean |err| <= 2e-3, lse max
+|err| <= 1e-3 against the unrounded oracle, on every (sequence, head, token)
+of every case, including the full-size decode workloads.  Queries that see
+no key must return o = 0 and lse = -inf exactly.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from exact_tiled_attention_attn_amd import attn
+from exact_tiled_attention_attn_amd.inputs import (decode_lengths, make_decode_q, make_paged_kv,
+                                                   to_f64)
+from exact_tiled_attention_attn_amd.workloads import DECODE_WORKLOADS
+from oracle import decode_paged
+
+pytestmark = pytest.mark.gpu
+
+O_MAX, O_MEAN, LSE_MAX = 2e-2, 2e-3, 1e-3
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    attn.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def run(q, kc, vc, table, lens, max_len, window=0, scale=None):
+    o, lse = attn.decode(q.to(DEV), kc.to(DEV), vc.to(DEV), table.to(DEV),
+                         torch.tensor(lens, dtype=torch.int32, device=DEV), max_len,
+                         window=window, scale=scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def check(o, lse, o_ref, l_ref, label):
+    lg = lse.double().numpy()
+    empty = ~np.isfinite(l_ref)
+    assert np.array_equal(np.isfinite(lg), ~empty), f"{label}: -inf pattern"
+    if empty.any():
+        assert not to_f64(o)[empty].any(), f"{label}: o of an empty query"
+    eo = np.abs(to_f64(o) - o_ref)[~empty]
+    el = np.abs(lg[~empty] - l_ref[~empty])
+    if eo.size == 0:
+        return
+    say(f"  {label}: max|dO|={eo.max():.3e} mean|dO|={eo.mean():.3e} max|dlse|={el.max():.3e}")
+    assert eo.max() <= O_MAX and eo.mean() <= O_MEAN and el.max() <= LSE_MAX, label
+
+
+CASES = [
+    # B, Hq, Hkv, T, d, page_size, lens, window
+    (1, 1, 1, 1, 128, 16, [1], 0),
+    (2, 2, 2, 1, 64, 16, [17, 5], 0),
+    (3, 8, 1, 1, 128, 16, [100, 33, 64], 0),          # multi-query
+    (2, 8, 2, 4, 128, 32, [300, 257], 0),             # GQA 4 x 4 tokens = 16 columns
+    (2, 64, 8, 4, 128, 64, [1000, 4097], 0),          # 32 columns
+    (4, 32, 32, 1, 128, 128, [5000, 1, 129, 2048], 0),
+    (2, 16, 2, 2, 64, 16, [777, 1500], 100),          # window
+    (2, 8, 8, 3, 128, 256, [2, 600], 1),              # window 1, more tokens than cache
+    (1, 4, 4, 1, 128, 4096, [9000], 0),               # large pages
+    (3, 4, 2, 8, 128, 16, [8, 7, 40], 5),             # T > L for one sequence
+    (2, 32, 4, 4, 128, 64, [70000, 3], 4096),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
+def test_decode_parity(case):
+    B, Hq, Hkv, T, d, ps, lens, window = case
+    say(f"case decode {case}")
+    kc, vc, table = make_paged_kv(lens, Hkv, d, ps, seed=100 + len(lens) + Hq)
+    q = make_decode_q(B, Hq, T, d, seed=200 + T)
+    max_len = max(lens)
+    o, lse = run(q, kc, vc, table, lens, max_len, window)
+    o_ref, l_ref = decode_paged(to_f64(q), to_f64(kc), to_f64(vc), table.numpy(), lens,
+                                1 / math.sqrt(d), window)
+    check(o, lse, o_ref, l_ref, str(case))
+
+
+def test_decode_split_choice_does_not_change_the_result_beyond_rounding():
+    """A larger max_seq_len changes the key split; results agree to rounding."""
+    lens = [3000, 1200]
+    kc, vc, table = make_paged_kv(lens, 2, 128, 64, seed=31)
+    q = make_decode_q(2, 16, 2, 128, seed=32)
+    a = run(q, kc, vc, table, lens, 3000)
+    b = run(q, kc, vc, table, lens, 3000 * 40)
+    assert (a[0].float() - b[0].float()).abs().max() <= 2 ** -7
+    assert (a[1] - b[1]).abs().max() <= 1e-5
+
+
+def test_decode_shared_pages_and_scale_sign():
+    lens = [200, 200]
+    kc, vc, table = make_paged_kv(lens, 2, 128, 16, seed=33)
+    table[1] = table[0]  # both sequences read the same pages
+    q = make_decode_q(2, 8, 1, 128, seed=34)
+    q[1] = q[0]
+    o, lse = run(q, kc, vc, table, lens, 200)
+    assert torch.equal(o[0], o[1]) and torch.equal(lse[0], lse[1])
+    for scale in (-0.0883883, 0.0, 0.7):
+        o, lse = run(q, kc, vc, table, lens, 200, scale=scale)
+        o_ref, l_ref = decode_paged(to_f64(q), to_f64(kc), to_f64(vc), table.numpy(), lens, scale)
+        check(o, lse, o_ref, l_ref, f"scale={scale}")
+
+
+def test_decode_deterministic_and_guard_bands():
+    lens = [900, 50, 333]
+    B, Hq, Hkv, T, d = 3, 8, 2, 2, 128
+    kc, vc, table = make_paged_kv(lens, Hkv, d, 32, seed=35)
+    q = make_decode_q(B, Hq, T, d, seed=36).to(DEV)
+    kc, vc, table = kc.to(DEV), vc.to(DEV), table.to(DEV)
+    lt = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    pad = 4096
+    res = []
+    for _ in range(2):
+        ob = torch.full((B * Hq * T * d + 2 * pad,), 7.0, dtype=torch.bfloat16, device=DEV)
+        lb = torch.full((B * Hq * T + 2 * pad,), 7.0, dtype=torch.float32, device=DEV)
+        o = ob[pad:pad + B * Hq * T * d].view(B, Hq, T, d)
+        lse = lb[pad:pad + B * Hq * T].view(B, Hq, T)
+        attn.decode(q, kc, vc, table, lt, 900, out=(o, lse))
+        torch.cuda.synchronize()
+        for buf, n in ((ob, B * Hq * T * d), (lb, B * Hq * T)):
+            assert bool((buf[:pad] == 7.0).all()) and bool((buf[pad + n:] == 7.0).all())
+        res.append((o.clone(), lse.clone()))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+@pytest.mark.parametrize("name", list(DECODE_WORKLOADS))
+def test_decode_workload_parity(name):
+    w = DECODE_WORKLOADS[name]
+    lens = decode_lengths(w.B, w.max_len, w.seed)
+    say(f"case decode workload {name} lens={lens[:8]}...")
+    kc, vc, table = make_paged_kv(lens, w.Hkv, w.d, w.page_size, seed=w.seed)
+    q = make_decode_q(w.B, w.Hq, w.T, w.d, seed=w.seed + 1)
+    o, lse = run(q, kc, vc, table, lens, w.max_len, w.window, w.sm_scale)
+    say("  HIP done; oracle")
+    o_ref, l_ref = decode_paged(to_f64(q), kc.float().numpy(), vc.float().numpy(), table.numpy(),
+                                lens, w.sm_scale, w.window)
+    check(o, lse, o_ref, l_ref, name)
