@@ -18,6 +18,10 @@ Contents
                by the chain rule; pinned by central finite differences of the
                forward oracle, by float64 autograd through masked SDPA and by
                closed forms.
+``general``    NumPy float64 attention over packed variable-length sequences
+               with causal / window / band / global-token masks; pinned by the
+               forward oracle per sequence, by a per-pair brute force and by
+               closed forms.
 ``decode``     NumPy float64 decode attention over a paged KV cache (gather
                through the page table, then the plain definition), and the
                rule that merges results over disjoint key sets; pinned by the
@@ -57,4 +61,5 @@ from .attention import (  # noqa: F401
 )
 from .backward import attention_backward  # noqa: F401
 from .decode import decode_paged, gather_pages, merge_partials  # noqa: F401
+from .general import attention_general, visible  # noqa: F401
 from .brute import brute_attention  # noqa: F401
