@@ -13,7 +13,9 @@ The same line also carries, as secondary figures, the backward (attn_bwd:
 dQ, dK, dV) timed on the same workload, at 10*d FLOPs per unmasked score
 (S, dP, dV, dQ, dK: five 2*d contractions), and the paged decode
 (attn_decode_paged) on the decode workloads in HBM GB/s (the visible K and V
-rows once, q, o, lse and the page-table entries).
+rows once, q, o, lse and the page-table entries), and the packed-sequence
+forward with structured masks (attn_fwd_varlen) at 4*d FLOPs per visible
+score.
 """
 
 from __future__ import annotations
@@ -35,6 +37,7 @@ OTHERS = ["c2_causal_mha_sharp", "c3_causal_window", "c4_causal_gqa", "c5_long_c
           "c5_long_window"]
 BWD_OTHERS = ["c4_causal_gqa"]
 DECODE = ["d1_decode_gqa_128k", "d2_decode_mha_8k", "d3_decode_window_spec4"]
+VARLEN = ["v1_packed_causal_gqa", "l1_longformer_4k"]
 KERNEL_SRC = os.path.join(ROOT, "exact_tiled_attention_attn_amd", "csrc", "attn_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -184,6 +187,44 @@ def time_decode(w, steps, warmup, torch, attn):
     return ev_ms, lens
 
 
+def time_varlen(w, steps, warmup, torch, attn):
+    """attn_fwd_varlen on a packed workload.  Returns event ms per call."""
+    from exact_tiled_attention_attn_amd.inputs import make_packed_qkv
+    q, k, v, cu = make_packed_qkv(list(w.lens), w.Hq, w.Hkv, w.d, seed=w.seed)
+    dev = torch.device("cuda:0")
+    q, k, v, cu = q.to(dev), k.to(dev), v.to(dev), cu.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.Hq, w.total), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    B, max_len = len(w.lens), max(w.lens)
+
+    def launch():
+        st = attn.attn_fwd_varlen(q, k, v, o, lse, cu, B, max_len, w.total, w.Hq, w.Hkv, w.d,
+                                  w.sm_scale, int(w.causal), w.window, w.radius, w.n_global,
+                                  stream)
+        if st != 0:
+            raise RuntimeError(f"attn_fwd_varlen: {attn.attn_status_string(st)}")
+
+    t_end = time.perf_counter() + 0.3
+    n = 0
+    while n < warmup or time.perf_counter() < t_end:
+        launch()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ev_ms = e0.elapsed_time(e1) / steps
+    del q, k, v, cu, o, lse
+    return ev_ms
+
+
 def cpu_baseline(w, host, seconds):
     """The float64 oracle on the host cores, on the same workload: the whole
     workload when it fits in about 2 * `seconds`, else a seeded sample of
@@ -286,6 +327,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-decode", action="store_true", help="skip the paged-decode timing")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the packed-sequence / structured-mask timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
@@ -300,9 +343,9 @@ def main():
 
     from exact_tiled_attention_attn_amd import attn
     from exact_tiled_attention_attn_amd.workloads import (DECODE_WORKLOADS, MI355X_BF16_DENSE_TFLOPS,
-                                                          MI355X_HBM_GBPS, WORKLOADS,
-                                                          algorithmic_bytes, bwd_flops,
-                                                          decode_bytes, flops)
+                                                          MI355X_HBM_GBPS, VARLEN_WORKLOADS,
+                                                          WORKLOADS, algorithmic_bytes, bwd_flops,
+                                                          decode_bytes, flops, varlen_flops)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
@@ -386,6 +429,18 @@ def main():
                         "ms": round(em, 4), "flops_per_call": bf}
             torch.cuda.empty_cache()
         out["backward"] = bw
+    if not args.no_varlen:
+        var = {}
+        for name in VARLEN if not args.no_others else VARLEN[:1]:
+            vw = VARLEN_WORKLOADS[name]
+            log(f"timing varlen {name}")
+            em = time_varlen(vw, args.steps, max(1, args.warmup // 2), torch, attn)
+            vf = varlen_flops(vw)
+            var[name] = {"tflops": round(vf / (em * 1e-3) / 1e12, 2),
+                         "pct_of_peak": round(100 * vf / (em * 1e-3) / 1e12 / peak, 2),
+                         "ms": round(em, 4), "flops_per_call": vf}
+            torch.cuda.empty_cache()
+        out["varlen"] = var
     if not args.no_decode:
         dec = {}
         for name in DECODE if not args.no_others else DECODE[:1]:

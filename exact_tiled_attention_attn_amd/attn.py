@@ -21,7 +21,7 @@ ATTN_ERR_UNSUPPORTED = 2
 ATTN_ERR_LAUNCH = 3
 ATTN_MAX_N = 1 << 22
 
-EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_bwd_workspace_size",
+EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_bwd", "attn_bwd_workspace_size",
             "attn_decode_paged", "attn_decode_workspace_size", "attn_num_variants",
             "attn_variant_name", "attn_status_string", "attn_abi_version")
 
@@ -51,6 +51,8 @@ def load_library():
     lib.attn_fwd.restype = i
     lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
     lib.attn_fwd_ex.restype = i
+    lib.attn_fwd_varlen.argtypes = [vp] * 6 + [i] * 6 + [f, i, i, i, i, vp]
+    lib.attn_fwd_varlen.restype = i
     lib.attn_bwd.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, i, vp]
     lib.attn_bwd.restype = i
     lib.attn_bwd_workspace_size.argtypes = [i, i, i]
@@ -110,6 +112,16 @@ def attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, window, varian
     return lib.attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(Hq),
                            int(Hkv), int(N), int(d), float(scale), int(causal), int(window),
                            int(variant), _stream(stream, q, k, v, o, lse))
+
+
+def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, max_seqlen, total_rows, Hq, Hkv, d, scale,
+                    causal, window, radius, n_global, stream=None):
+    """Call the C packed-sequence forward; returns its status code."""
+    lib = load_library()
+    return lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
+                               int(B), int(max_seqlen), int(total_rows), int(Hq), int(Hkv),
+                               int(d), float(scale), int(causal), int(window), int(radius),
+                               int(n_global), _stream(stream, q, k, v, o, lse))
 
 
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, scale, causal,
@@ -282,4 +294,42 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, window=0, sc
                            scale, int(window), stream)
     if st != ATTN_OK:
         raise AttnError(f"attn_decode_paged failed: {attn_status_string(st)} (status {st})", st)
+    return o, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, window=0, radius=0, n_global=0,
+               scale=None, out=None, stream=None):
+    """Packed-sequence forward with structured masks; raises on any error.
+
+    q: (Hq, total, d) bf16; k, v: (Hkv, total, d) bf16; cu_seqlens: (B + 1,)
+    int32 on the device.  Returns o (Hq, total, d) bf16 and lse (Hq, total)
+    fp32.
+    """
+    import torch
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
+                        ("v", v, torch.bfloat16), ("cu_seqlens", cu_seqlens, torch.int32)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise AttnError(f"{name} must be a CUDA (HIP) tensor")
+        if t.dtype != dt:
+            raise AttnError(f"{name} must be {dt}")
+        if not t.is_contiguous():
+            raise AttnError(f"{name} must be contiguous")
+    if q.dim() != 3 or k.dim() != 3 or cu_seqlens.dim() != 1:
+        raise AttnError("q (Hq, total, d), k, v (Hkv, total, d), cu_seqlens (B + 1,)")
+    Hq, total, d = q.shape
+    Hkv = k.shape[0]
+    if tuple(k.shape) != (Hkv, total, d) or tuple(v.shape) != tuple(k.shape):
+        raise AttnError("k and v must be (Hkv, total, d) matching q")
+    B = cu_seqlens.shape[0] - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((Hq, total), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    st = attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, max_seqlen, total, Hq, Hkv, d, scale,
+                         int(bool(causal)), int(window), int(radius), int(n_global), stream)
+    if st != ATTN_OK:
+        raise AttnError(f"attn_fwd_varlen failed: {attn_status_string(st)} (status {st})", st)
     return o, lse

@@ -53,6 +53,23 @@ attn_status_t validate_bwd(const attn::BwdProblem &p) {
   return ATTN_OK;
 }
 
+attn_status_t validate_varlen(const attn::VarlenProblem &p) {
+  if (p.B < 0 || p.max_seqlen < 0 || p.total_rows < 0 || p.radius < 0 || p.n_global < 0)
+    return ATTN_ERR_INVALID_ARG;
+  if (p.Hq < 1 || p.Hkv < 1 || p.Hq % p.Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (p.causal != 0 && p.causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(p.scale)) return ATTN_ERR_INVALID_ARG;
+  if (p.d != 64 && p.d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (p.window > 0 && p.causal == 0) return ATTN_ERR_UNSUPPORTED;
+  if (p.max_seqlen > ATTN_MAX_N) return ATTN_ERR_UNSUPPORTED;
+  if (p.B == 0 || p.max_seqlen == 0 || p.total_rows == 0) return ATTN_OK;
+  if (!p.q || !p.k || !p.v || !p.o || !p.lse || !p.cu_seqlens) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(p.q) || !aligned16(p.k) || !aligned16(p.v) || !aligned16(p.o) ||
+      !aligned16(p.lse) || (reinterpret_cast<uintptr_t>(p.cu_seqlens) & 3u) != 0)
+    return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
 bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 
 attn_status_t validate_decode(const attn::DecodeProblem &p) {
@@ -100,6 +117,23 @@ attn_status_t attn_fwd(const void *q, const void *k, const void *v, void *o, flo
                        void *stream) {
   return attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, window, attn::kAuto,
                      stream);
+}
+
+attn_status_t attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                              const int *cu_seqlens, int B, int max_seqlen, int total_rows,
+                              int Hq, int Hkv, int d, float scale, int causal, int window,
+                              int radius, int n_global, void *stream) {
+  attn::VarlenProblem p{q,  k,  v,   o,   lse,   cu_seqlens, B,      max_seqlen, total_rows,
+                        Hq, Hkv, d, scale, causal, window, radius, n_global};
+  const attn_status_t st = validate_varlen(p);
+  if (st != ATTN_OK) return st;
+  if (B == 0 || max_seqlen == 0 || total_rows == 0) return ATTN_OK;
+  if (p.window >= max_seqlen) p.window = 0;
+  if (p.radius >= max_seqlen) p.radius = 0;
+  if (p.n_global > max_seqlen) p.n_global = max_seqlen;
+  const hipError_t e = attn::launch_fwd_varlen(p, static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidValue) return ATTN_ERR_UNSUPPORTED;
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 size_t attn_bwd_workspace_size(int B, int Hq, int N) {

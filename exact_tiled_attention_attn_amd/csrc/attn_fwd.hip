@@ -87,6 +87,14 @@ struct Params {
   int neg;        // scale < 0: Q is negated on load, exact in bf16
   int causal;
   int window;     // 0: none
+  // packed variable-length batches and local + global masks (GEN kernels
+  // only): sequence b is rows cu[b] .. cu[b+1]-1 of every head's
+  // [total_rows][D] slice; query and key rows below nglob are global; a
+  // radius > 0 limits the others to |i - j| <= radius
+  const int *cu;
+  int total_rows;
+  int radius;
+  int nglob;
 };
 
 template <int D>
@@ -167,24 +175,73 @@ __device__ __forceinline__ float wave_sum_pair(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
+// The key tiles a block of query rows visits: [0, a_hi) then [b_lo, b_hi)
+// (disjoint, a_hi < b_lo).  The first range holds the global keys, the
+// second the causal / window / radius band; a block holding a global row
+// visits every key it may see.  Without global tokens it is one range.
+struct Segs {
+  int a_hi, b_lo, b_hi;
+  __device__ __forceinline__ int count() const { return a_hi + max(b_hi - b_lo, 0); }
+  __device__ __forceinline__ int tile(int k) const { return k < a_hi ? k : b_lo + (k - a_hi); }
+  __device__ __forceinline__ bool has(int t) const { return t < a_hi || (t >= b_lo && t < b_hi); }
+};
+
+// Rows [r0, r1) of a sequence of N rows (r0 < r1 <= N).
+__device__ __forceinline__ Segs key_segments(const Params &prm, int r0, int r1, int N) {
+  const int hi_c = prm.causal ? r1 : N;  // keys past this are never seen
+  Segs sg;
+  if (r0 < prm.nglob) {  // a global row sees every key it may
+    sg.a_hi = 0;
+    sg.b_lo = 0;
+    sg.b_hi = (hi_c + kBN - 1) / kBN;
+    return sg;
+  }
+  int lo = 0, hi = hi_c;
+  if (prm.window > 0) lo = max(lo, r0 - prm.window + 1);
+  if (prm.radius > 0) {
+    lo = max(lo, r0 - prm.radius);
+    hi = min(hi, r1 + prm.radius);
+  }
+  sg.a_hi = (min(prm.nglob, hi_c) + kBN - 1) / kBN;
+  sg.b_lo = lo / kBN;
+  sg.b_hi = (hi + kBN - 1) / kBN;
+  if (sg.b_lo <= sg.a_hi) {  // the ranges touch: one range
+    sg.a_hi = max(sg.a_hi, sg.b_hi);
+    sg.b_lo = sg.b_hi = sg.a_hi;
+  }
+  return sg;
+}
+
 // Which (batch, head, rows, key tiles) a wave of a workgroup owns.
 struct Task {
   int b, head, kvh;
+  int N;               // rows of this sequence
   int qw0;             // first query row of this wave
-  int wg_lo, wg_hi;    // key tiles any row of the workgroup sees
-  int w_lo, w_hi;      // key tiles any row of this wave sees
-  size_t q_slice;      // (b * Hq + head) * N: first row of the Q / O slice
-  size_t kv_slice;     // (b * Hkv + kvh) * N: first row of the K / V slice
+  Segs wg;             // key tiles any row of the workgroup sees
+  Segs w;              // key tiles any row of this wave sees
+  size_t q_slice;      // first row of the Q / O slice
+  size_t kv_slice;     // first row of the K / V slice
+  bool empty;          // no row of the workgroup lies inside its sequence
 };
 
 // kRows query rows per workgroup, P heads per workgroup (wave w serves head
-// w % P on rows (w / P) * 32 ..).
-template <int P, int kRows>
+// w % P on rows (w / P) * 32 ..).  GEN: packed sequences [cu[b], cu[b+1]).
+template <int P, int kRows, bool GEN>
 __device__ __forceinline__ Task make_task(const Params &prm, int wave) {
   Task tk;
-  const int logical = xcd_remap(blockIdx.x, prm.total);
-  const int qrank = logical % prm.nq;
-  const int hgb = logical / prm.nq;
+  int qrank, hgb;
+  if constexpr (GEN) {
+    // packed sequences of different lengths: tile rank slowest, so the
+    // heaviest tiles of every sequence go first and consecutive workgroups
+    // (dealt round-robin to the XCDs) spread every sequence over all XCDs
+    const int nbh = prm.B * prm.groups;
+    qrank = blockIdx.x / nbh;
+    hgb = blockIdx.x % nbh;
+  } else {
+    const int logical = xcd_remap(blockIdx.x, prm.total);
+    qrank = logical % prm.nq;
+    hgb = logical / prm.nq;
+  }
   const int hg = hgb % prm.groups;
   tk.b = hgb / prm.groups;
   const int qi = prm.causal ? (prm.nq - 1 - qrank) : qrank;  // heaviest tiles first
@@ -192,19 +249,28 @@ __device__ __forceinline__ Task make_task(const Params &prm, int wave) {
   tk.kvh = __builtin_amdgcn_readfirstlane((hg * P) / prm.G);  // P divides G
   const int wg_r0 = qi * kRows;
   tk.qw0 = wg_r0 + (wave / P) * 32;
-  const int N = prm.N;
-  auto tile_range = [&](int r0, int r1, int &lo, int &hi) {  // rows [r0, r1)
-    hi = prm.causal ? min(prm.nkt, (r1 - 1) / kBN + 1) : prm.nkt;
-    lo = prm.window > 0 ? max(0, r0 - prm.window + 1) / kBN : 0;
-  };
-  tile_range(wg_r0, min(N, wg_r0 + kRows), tk.wg_lo, tk.wg_hi);
-  if (tk.qw0 < N) {
-    tile_range(tk.qw0, min(N, tk.qw0 + 32), tk.w_lo, tk.w_hi);
+  int N;
+  if constexpr (GEN) {
+    // offsets clamped into [0, total_rows]: an inconsistent table yields
+    // empty or shortened sequences, never reads outside the tensors
+    const int start = min(max(prm.cu[tk.b], 0), prm.total_rows);
+    N = min(prm.cu[tk.b + 1], prm.total_rows) - start;
+    tk.kv_slice = (size_t)tk.kvh * prm.total_rows + start;
+    tk.q_slice = (size_t)tk.head * prm.total_rows + start;
   } else {
-    tk.w_lo = tk.w_hi = 0;  // rows past the end: this wave only helps load tiles
+    N = prm.N;
+    tk.kv_slice = (size_t)(tk.b * prm.Hkv + tk.kvh) * N;
+    tk.q_slice = (size_t)(tk.b * prm.Hq + tk.head) * N;
   }
-  tk.kv_slice = (size_t)(tk.b * prm.Hkv + tk.kvh) * N;
-  tk.q_slice = (size_t)(tk.b * prm.Hq + tk.head) * N;
+  tk.N = N;
+  tk.empty = wg_r0 >= N;
+  if (tk.empty) return tk;
+  tk.wg = key_segments(prm, wg_r0, min(N, wg_r0 + kRows), N);
+  if (tk.qw0 < N) {
+    tk.w = key_segments(prm, tk.qw0, min(N, tk.qw0 + 32), N);
+  } else {
+    tk.w = Segs{0, 0, 0};  // rows past the end: this wave only helps load tiles
+  }
   return tk;
 }
 
@@ -216,7 +282,7 @@ __device__ __forceinline__ void load_q(const Params &prm, const Task &tk, int l3
   const uint16_t *qp = prm.q + tk.q_slice * D + (size_t)row * D + 8 * hh;
 #pragma unroll
   for (int kk = 0; kk < Geo<D>::kKSteps; ++kk) {
-    qf[kk] = row < prm.N ? *(const bf16x8 *)(qp + 16 * kk) : bf16x8{};
+    qf[kk] = row < tk.N ? *(const bf16x8 *)(qp + 16 * kk) : bf16x8{};
     if (prm.neg) {
       u32x4 t = __builtin_bit_cast(u32x4, qf[kk]);
       t ^= 0x80008000u;
@@ -266,15 +332,14 @@ struct RowState {
 // Whether key tile j0 holds a (row, key) pair that a row of the wave's 32
 // rows qw0.. cannot see: the causal diagonal, the window edge and the tile
 // holding key N - 1.  Wave-uniform.
-__device__ __forceinline__ bool tile_needs_mask(const Params &prm, int j0, int qw0) {
+__device__ __forceinline__ bool tile_needs_mask(const Params &prm, int j0, int qw0, int N) {
   return (prm.causal && j0 + kBN - 1 > qw0) ||
-         (prm.window > 0 && j0 <= qw0 + 31 - prm.window) || (j0 + kBN > prm.N);
+         (prm.window > 0 && j0 <= qw0 + 31 - prm.window) || (j0 + kBN > N);
 }
 
 // Scores of keys this lane's row cannot see become -inf (no branches).
 __device__ __forceinline__ void apply_mask(f32x16 (&s)[2], const Params &prm, int j0, int qw0,
-                                           int l32, int hh) {
-  const int N = prm.N;
+                                           int l32, int hh, int N) {
   // Register r of block rb holds key kbase + off with the compile-time
   // off = 32*rb + 8*(r/4) + r%4.  The keys this lane's row sees form the
   // range lo < off <= hi relative to kbase, so one unsigned compare per
@@ -297,9 +362,57 @@ __device__ __forceinline__ void apply_mask(f32x16 (&s)[2], const Params &prm, in
   }
 }
 
+// The general rule of the GEN kernels: row i sees key j < N iff
+//   (not causal or j <= i) and (i < nglob or j < nglob or
+//    ((window <= 0 or j > i - window) and (radius <= 0 or |i - j| <= radius))).
+__device__ __forceinline__ bool tile_needs_mask_gen(const Params &prm, int j0, int qw0, int N) {
+  if (j0 + kBN > N || (prm.causal && j0 + kBN - 1 > qw0)) return true;
+  if (qw0 + 31 < prm.nglob || j0 + kBN - 1 < prm.nglob) return false;
+  const bool win_ok = prm.window <= 0 || j0 > qw0 + 31 - prm.window;
+  const bool rad_ok = prm.radius <= 0 ||
+                      (j0 >= qw0 + 31 - prm.radius && j0 + kBN - 1 <= qw0 + prm.radius);
+  return !(win_ok && rad_ok);
+}
+
+// The keys row i sees are two ranges: the global keys [0, gcap) and the
+// local range [lo, hi] (for a global row: every key it may see).  With the
+// per-register offset off (key = kbase + off), each is one unsigned compare.
+__device__ __forceinline__ void apply_mask_gen(f32x16 (&s)[2], const Params &prm, int j0,
+                                               int qw0, int l32, int hh, int N) {
+  const int i = qw0 + l32;
+  const int hi_c = prm.causal ? min(i, N - 1) : N - 1;  // last key causality allows
+  int lo = 0, hi = hi_c;
+  if (i >= prm.nglob) {
+    if (prm.window > 0) lo = max(lo, i - prm.window + 1);
+    if (prm.radius > 0) {
+      lo = max(lo, i - prm.radius);
+      hi = min(hi, i + prm.radius);
+    }
+  }
+  const int gcap = min(prm.nglob, hi_c + 1);
+  const int kbase = j0 + 4 * hh;
+  const int a = kbase - lo;                       // key - lo = off + a
+  const unsigned span = (unsigned)max(hi - lo + 1, 0);
+  const unsigned gspan = (unsigned)max(gcap, 0);  // key < gcap
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int off = 32 * rb + 8 * (r >> 2) + (r & 3);
+      const bool vis = (unsigned)(off + a) < span || (unsigned)(off + kbase) < gspan;
+      s[rb][r] = vis ? s[rb][r] : -INFINITY;
+    }
+  }
+}
+
+template <bool GEN>
 __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], const Params &prm, int j0, int qw0,
-                                          int l32, int hh) {
-  if (tile_needs_mask(prm, j0, qw0)) apply_mask(s, prm, j0, qw0, l32, hh);
+                                          int l32, int hh, int N) {
+  if constexpr (GEN) {
+    if (tile_needs_mask_gen(prm, j0, qw0, N)) apply_mask_gen(s, prm, j0, qw0, l32, hh, N);
+  } else {
+    if (tile_needs_mask(prm, j0, qw0, N)) apply_mask(s, prm, j0, qw0, l32, hh, N);
+  }
 }
 
 // Online softmax of one tile of scores (scaled log2 domain), without
@@ -380,7 +493,7 @@ __device__ __forceinline__ void write_out(const Params &prm, const Task &tk, int
   const float ltot = wave_sum_pair(st.lsum);
   const float lrtot = wave_sum_pair(st.lrnd);
   const int row = tk.qw0 + l32;
-  if (row >= prm.N) return;
+  if (row >= tk.N) return;
   const float inv = 1.0f / lrtot;
   uint16_t *op = prm.o + tk.q_slice * D + (size_t)row * D + 4 * hh;
 #pragma unroll
@@ -400,7 +513,7 @@ __device__ __forceinline__ void write_out(const Params &prm, const Task &tk, int
 // Lockstep schedule: per key tile, every wave computes S, softmax and PV
 // between two workgroup barriers.
 // ---------------------------------------------------------------------------
-template <int D, int NW, int P>
+template <int D, int NW, int P, bool GEN>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
   using g = Geo<D>;
   constexpr int kRows = 32 * NW / P;  // query rows per workgroup
@@ -415,8 +528,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
 
-  const Task tk = make_task<P, kRows>(prm, wave);
-  const int N = prm.N;
+  const Task tk = make_task<P, kRows, GEN>(prm, wave);
+  if (tk.empty) return;  // the whole workgroup: its tile lies past its sequence
+  const int N = tk.N;
   const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(prm.k + tk.kv_slice * D, (uint32_t)N * D * 2);
   const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(prm.v + tk.kv_slice * D, (uint32_t)N * D * 2);
 
@@ -432,8 +546,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
   const float c = prm.c;
 
   TileStage<D, NW> stage;
-  if (tk.wg_lo < tk.wg_hi) {
-    stage.load(rs_k, rs_v, tk.wg_lo * kBN, tk.wg_lo * kBN, tid);
+  const int count = tk.wg.count();
+  if (count > 0) {
+    const int t0 = tk.wg.tile(0);
+    stage.load(rs_k, rs_v, t0 * kBN, t0 * kBN, tid);
     stage.store(set0, set0 + g::kKTileB, tid);
   }
   __syncthreads();
@@ -476,7 +592,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
     for (int i = 0; i < kVA; ++i) va[i] = vf(i);
     __builtin_amdgcn_sched_barrier(0);
 
-    mask_tile(s, prm, t * kBN, tk.qw0, l32, hh);
+    mask_tile<GEN>(s, prm, t * kBN, tk.qw0, l32, hh, N);
     bf16x8 pf[2][2];
     softmax_tile<g::kDB>(s, pf, st, oacc, c);
 
@@ -496,17 +612,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
   // one from LDS (if this wave sees any of its keys), then park the next tile
   // in the other buffer set.  The register loads are only waited for at that
   // final store, so they overlap the whole tile's compute.
-  auto step = [&](const int t, lchar *const cur_set, lchar *const next_set) {
-    const bool more = t + 1 < tk.wg_hi;
-    if (more) stage.load(rs_k, rs_v, (t + 1) * kBN, (t + 1) * kBN, tid);
-    if (t >= tk.w_lo && t < tk.w_hi) compute(t, cur_set);
+  auto step = [&](const int k, lchar *const cur_set, lchar *const next_set) {
+    const bool more = k + 1 < count;
+    if (more) {
+      const int tn = tk.wg.tile(k + 1);
+      stage.load(rs_k, rs_v, tn * kBN, tn * kBN, tid);
+    }
+    const int t = tk.wg.tile(k);
+    if (tk.w.has(t)) compute(t, cur_set);
     if (more) stage.store(next_set, next_set + g::kKTileB, tid);
     __syncthreads();
   };
 
-  for (int t = tk.wg_lo; t < tk.wg_hi; t += 2) {
-    step(t, set0, set1);
-    if (t + 1 < tk.wg_hi) step(t + 1, set1, set0);
+  for (int k = 0; k < count; k += 2) {
+    step(k, set0, set1);
+    if (k + 1 < count) step(k + 1, set1, set0);
   }
 
   write_out<D>(prm, tk, l32, hh, oacc, st);
@@ -515,7 +635,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
 template <int D, int NW, int P>
 hipError_t launch_t(const FwdProblem &p, hipStream_t stream) {
   constexpr int kRows = 32 * NW / P;
-  Params prm;
+  Params prm{};
   prm.q = static_cast<const uint16_t *>(p.q);
   prm.k = static_cast<const uint16_t *>(p.k);
   prm.v = static_cast<const uint16_t *>(p.v);
@@ -535,8 +655,49 @@ hipError_t launch_t(const FwdProblem &p, hipStream_t stream) {
   prm.causal = p.causal;
   prm.window = p.window;
   void *args[] = {&prm};
-  return hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_kernel<D, NW, P>),
+  return hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_kernel<D, NW, P, false>),
                          dim3(prm.total), dim3(NW * 64), args, 0, stream);
+}
+
+template <int D, int P>
+hipError_t launch_gen_t(const VarlenProblem &p, hipStream_t stream) {
+  constexpr int NW = 8;
+  constexpr int kRows = 32 * NW / P;
+  Params prm{};
+  prm.q = static_cast<const uint16_t *>(p.q);
+  prm.k = static_cast<const uint16_t *>(p.k);
+  prm.v = static_cast<const uint16_t *>(p.v);
+  prm.o = static_cast<uint16_t *>(p.o);
+  prm.lse = p.lse;
+  prm.B = p.B; prm.Hq = p.Hq; prm.Hkv = p.Hkv; prm.N = p.max_seqlen;
+  prm.G = p.Hq / p.Hkv;
+  prm.groups = p.Hq / P;
+  prm.nq = (p.max_seqlen + kRows - 1) / kRows;
+  const long long total = (long long)p.B * prm.groups * prm.nq;
+  if (total > 0x7fffffffLL) return hipErrorInvalidValue;
+  prm.total = (int)total;
+  prm.nkt = (p.max_seqlen + kBN - 1) / kBN;
+  const float c = std::fabs(p.scale) * kLog2e;
+  prm.c = c < FLT_MIN ? FLT_MIN : c;
+  prm.neg = p.scale < 0.0f ? 1 : 0;
+  prm.causal = p.causal;
+  prm.window = p.window;
+  prm.cu = p.cu_seqlens;
+  prm.total_rows = p.total_rows;
+  prm.radius = p.radius;
+  prm.nglob = p.n_global;
+  void *args[] = {&prm};
+  return hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_kernel<D, NW, P, true>),
+                         dim3(prm.total), dim3(NW * 64), args, 0, stream);
+}
+
+template <int D>
+hipError_t launch_gen_d(const VarlenProblem &p, hipStream_t stream) {
+  const int G = p.Hq / p.Hkv;
+  if (G % 8 == 0) return launch_gen_t<D, 8>(p, stream);
+  if (G % 4 == 0) return launch_gen_t<D, 4>(p, stream);
+  if (G % 2 == 0) return launch_gen_t<D, 2>(p, stream);
+  return launch_gen_t<D, 1>(p, stream);
 }
 
 template <int D, int NW>
@@ -568,6 +729,10 @@ const char *variant_name(int variant) {
 hipError_t launch_fwd(const FwdProblem &p, int variant, hipStream_t stream) {
   const int v = variant == kAuto ? kWaves8 : variant;
   return p.d == 128 ? launch_d<128>(p, v, stream) : launch_d<64>(p, v, stream);
+}
+
+hipError_t launch_fwd_varlen(const VarlenProblem &p, hipStream_t stream) {
+  return p.d == 128 ? launch_gen_d<128>(p, stream) : launch_gen_d<64>(p, stream);
 }
 
 }  // namespace attn

@@ -33,6 +33,21 @@ const char *variant_name(int variant);
 // the launch call (hipSuccess when it was enqueued).
 hipError_t launch_fwd(const FwdProblem &p, int variant, hipStream_t stream);
 
+// One packed variable-length forward problem with the general mask,
+// already validated.  Rows of sequence b: cu_seqlens[b] .. cu_seqlens[b+1]-1
+// (device array) of each head's [total_rows][d] slice.
+struct VarlenProblem {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  const int *cu_seqlens;
+  int B, max_seqlen, total_rows, Hq, Hkv, d;
+  float scale;
+  int causal, window, radius, n_global;
+};
+
+hipError_t launch_fwd_varlen(const VarlenProblem &p, hipStream_t stream);
+
 // One backward problem, already validated by the entry point.
 struct BwdProblem {
   const void *q, *k, *v, *o, *dout;

@@ -14,6 +14,10 @@ per-slice drawing keeps host memory bounded at the longest shapes.
 The upstream gradient dO of the backward is drawn the same way, from its own
 seed, as one (B, Hq, N, d) tensor of N(0, 1) values rounded to bfloat16.
 
+Packed variable-length batches (``make_packed_qkv``): Q, K, V of the whole
+packed batch drawn like the dense tensors, one (total, d) slice per head;
+the lengths of the workloads are seeded uniform integers.
+
 Paged decode inputs: per sequence b, its L_b cached tokens are drawn like K
 and V (one (L_b, Hkv, d) slice each, N(0, 1) rounded to bf16) and written
 into pages of a cache whose physical pages are a seeded random permutation
@@ -51,6 +55,19 @@ def make_dout(B: int, Hq: int, N: int, d: int, seed: int) -> torch.Tensor:
     """Return a bf16 CPU tensor dO shaped (B, Hq, N, d)."""
     gen = torch.Generator().manual_seed(int(seed))
     return _draw(gen, B, Hq, N, d)
+
+
+def make_packed_qkv(lens, Hq: int, Hkv: int, d: int, seed: int):
+    """Packed sequences: bf16 CPU tensors q (Hq, total, d), k and v
+    (Hkv, total, d), and cu_seqlens (B + 1,) int32; each head's rows drawn as
+    one (total, d) slice, in the order Q, K, V."""
+    total = int(sum(lens))
+    gen = torch.Generator().manual_seed(int(seed))
+    q = _draw(gen, 1, Hq, total, d)[0]
+    k = _draw(gen, 1, Hkv, total, d)[0]
+    v = _draw(gen, 1, Hkv, total, d)[0]
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32)
+    return q, k, v, cu
 
 
 def decode_lengths(B: int, max_len: int, seed: int) -> list[int]:

@@ -138,3 +138,72 @@ DECODE_WORKLOADS = {
     "d3_decode_window_spec4": DecodeWorkload("d3_decode_window_spec4", 8, 64, 8, 4, 128, 256,
                                              131072, 23, window=4096),
 }
+
+
+# ---------------------------------------------------------------------------
+# Packed variable-length batches with structured masks (block-diagonal
+# packing; Longformer band + global tokens).  Shapes: a packed batch of
+# documents with a seeded uniform length mix at the 32 / 8 GQA heads, d = 128;
+# Longformer at its 4096-token inputs, band 512 (radius 256), a handful (16)
+# of global tokens, 12 heads of d = 64.
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class VarlenWorkload:
+    name: str
+    lens: tuple
+    Hq: int
+    Hkv: int
+    d: int
+    causal: bool
+    window: int = 0
+    radius: int = 0
+    n_global: int = 0
+    seed: int = 0
+
+    @property
+    def sm_scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def total(self) -> int:
+        return sum(self.lens)
+
+
+def visible_pairs_general(N: int, causal: bool, window: int, radius: int, n_global: int) -> int:
+    """(row, key) pairs a sequence of N rows sees under the structured-mask
+    rule (global rows see every key they may; other rows the global keys
+    plus the band), by intervals per row."""
+    total = 0
+    for i in range(N):
+        hi_c = i + 1 if causal else N
+        if i < n_global:
+            total += hi_c
+            continue
+        lo, hi = 0, hi_c
+        if window > 0:
+            lo = max(lo, i - window + 1)
+        if radius > 0:
+            lo = max(lo, i - radius)
+            hi = min(hi, i + radius + 1)
+        total += max(0, hi - lo) + max(0, min(n_global, hi_c, lo))
+    return total
+
+
+def varlen_flops(w: VarlenWorkload) -> int:
+    return 4 * w.d * w.Hq * sum(visible_pairs_general(L, w.causal, w.window, w.radius,
+                                                      w.n_global) for L in w.lens)
+
+
+def _lens(B: int, max_len: int, seed: int) -> tuple:
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    return tuple(int(x) for x in rng.integers(1, max_len + 1, size=B))
+
+
+VARLEN_WORKLOADS = {
+    "v1_packed_causal_gqa": VarlenWorkload("v1_packed_causal_gqa", _lens(16, 8192, 31), 32, 8,
+                                           128, True, seed=31),
+    "l1_longformer_4k": VarlenWorkload("l1_longformer_4k", (4096,) * 8, 12, 12, 64, False,
+                                       radius=256, n_global=16, seed=32),
+}

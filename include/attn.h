@@ -1,6 +1,7 @@
 /*
  * attn.h -- C ABI of the MI355X (gfx950) exact tiled attention: the forward
- * pass, its gradients, and decode over a paged KV cache.
+ * pass (dense, and packed variable-length with structured masks), its
+ * gradients, and decode over a paged KV cache.
  *
  * Operation.  For every batch b, query head h and query row i
  *
@@ -95,6 +96,41 @@ attn_status_t attn_fwd(const void *q, const void *k, const void *v, void *o, flo
 attn_status_t attn_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
                           int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                           int window, int variant, void *stream);
+
+/* Forward over packed sequences of different lengths with structured masks.
+ *
+ * Block-diagonal packing: "Efficient attention: long context and
+ * sub-quadratic variants" (section "Against the real libraries") names
+ * xformers' BlockDiagonalMask among the masks that reach a kernel as
+ * iteration bounds: sequence b is rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of
+ * every head's slice and attends only within itself.  Local plus global
+ * attention (Longformer; same page, "Sliding-window and local attention",
+ * and "Efficient Attention: FlashAttention, Sparse, Linear", 45.2.2): a
+ * band of half-width `radius` around each token, and `n_global` global
+ * tokens -- the first n_global positions of each sequence -- that attend
+ * to, and are attended by, every token.  Within a sequence, row i sees key
+ * j iff
+ *     (causal == 0 || j <= i) &&
+ *     (i < n_global || j < n_global ||
+ *      ((window <= 0 || j > i - window) && (radius <= 0 || |i - j| <= radius)))
+ * The kernel visits only the key tiles of the global keys and of the band.
+ *
+ *   q           bf16 [Hq][total_rows][d]     (head-major, sequences packed)
+ *   k, v        bf16 [Hkv][total_rows][d]
+ *   o           bf16 [Hq][total_rows][d]     written
+ *   lse         fp32 [Hq][total_rows]        written
+ *   cu_seqlens  int32 [B + 1], device memory, 0 = cu[0] <= ... <= cu[B] =
+ *               total_rows, every length <= max_seqlen (not checked: the
+ *               host never reads it)
+ *   max_seqlen  host-side bound of the lengths (sizes the grid)
+ *   radius, n_global  >= 0 (0: none); window as for attn_fwd
+ * Errors as for attn_fwd (negative radius, n_global, total_rows -> invalid
+ * argument; cu_seqlens not 4-byte aligned -> unsupported).  B == 0,
+ * max_seqlen == 0 or total_rows == 0 launches nothing. */
+attn_status_t attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                              const int *cu_seqlens, int B, int max_seqlen, int total_rows,
+                              int Hq, int Hkv, int d, float scale, int causal, int window,
+                              int radius, int n_global, void *stream);
 
 /* Backward pass: the gradients of a loss L with respect to q, k and v, given
  * dout = dL/do for the forward above.  "Efficient attention: long context
@@ -197,7 +233,7 @@ const char *attn_variant_name(int variant);
 const char *attn_status_string(attn_status_t status);
 
 /* ABI version of this header (incremented on any signature change). */
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 int attn_abi_version(void);
 
 #ifdef __cplusplus

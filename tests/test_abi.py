@@ -224,3 +224,38 @@ def test_decode_workspace_size(lib):
     # the split never exceeds 64 page-table entries
     n16 = attn.attn_decode_workspace_size(1, 1, 1, 1, 64, 16, 1 << 20)
     assert n16 // ((64 + 1) * 4) >= (1 << 20) // (64 * 16)
+
+
+VAR_GOOD = dict(q=P, k=P, v=P, o=P, lse=P, cu_seqlens=P, B=2, max_seqlen=64, total_rows=100, Hq=4,
+                Hkv=2, d=128, scale=0.1, causal=0, window=0, radius=16, n_global=2)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(cu_seqlens=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(lse=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(B=-1), attn.ATTN_ERR_INVALID_ARG),
+    (dict(total_rows=-1), attn.ATTN_ERR_INVALID_ARG),
+    (dict(radius=-1), attn.ATTN_ERR_INVALID_ARG),
+    (dict(n_global=-3), attn.ATTN_ERR_INVALID_ARG),
+    (dict(Hq=3), attn.ATTN_ERR_INVALID_ARG),
+    (dict(causal=5), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), attn.ATTN_ERR_INVALID_ARG),
+    (dict(d=32), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(window=8), attn.ATTN_ERR_UNSUPPORTED),          # window needs causal
+    (dict(cu_seqlens=P + 2), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(k=P + 8), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(max_seqlen=(1 << 22) + 1), attn.ATTN_ERR_UNSUPPORTED),
+])
+def test_varlen_rejects_bad_arguments_without_launching(lib, kw, expect):
+    a = dict(VAR_GOOD)
+    a.update(kw)
+    assert attn.attn_fwd_varlen(**a) == expect
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(max_seqlen=0), dict(total_rows=0),
+                                dict(B=0, q=0, k=0, v=0, o=0, lse=0, cu_seqlens=0)])
+def test_varlen_empty_problem_is_ok_and_launches_nothing(lib, kw):
+    a = dict(VAR_GOOD)
+    a.update(kw)
+    assert attn.attn_fwd_varlen(**a) == attn.ATTN_OK
