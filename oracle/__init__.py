@@ -22,6 +22,10 @@ Contents
                with causal / window / band / global-token masks; pinned by the
                forward oracle per sequence, by a per-pair brute force and by
                closed forms.
+``fp8``        OCP E4M3 rounding, byte codes and power-of-two per-tensor
+               scales, and the exact attention of the dequantised tensors;
+               pinned by the format's closed-form values, a brute-force
+               nearest search with ties to even, and torch's float8_e4m3fn.
 ``decode``     NumPy float64 decode attention over a paged KV cache (gather
                through the page table, then the plain definition), and the
                rule that merges results over disjoint key sets; pinned by the
@@ -62,4 +66,5 @@ from .attention import (  # noqa: F401
 from .backward import attention_backward  # noqa: F401
 from .decode import decode_paged, gather_pages, merge_partials  # noqa: F401
 from .general import attention_general, visible  # noqa: F401
+from . import fp8  # noqa: F401
 from .brute import brute_attention  # noqa: F401
