@@ -15,7 +15,7 @@ dQ, dK, dV) timed on the same workload, at 10*d FLOPs per unmasked score
 (attn_decode_paged) on the decode workloads in HBM GB/s (the visible K and V
 rows once, q, o, lse and the page-table entries), and the packed-sequence
 forward with structured masks (attn_fwd_varlen) at 4*d FLOPs per visible
-score.
+score, and the FP8 forward (attn_fwd_fp8) against the dense fp8 peak.
 """
 
 from __future__ import annotations
@@ -38,6 +38,7 @@ OTHERS = ["c2_causal_mha_sharp", "c3_causal_window", "c4_causal_gqa", "c5_long_c
 BWD_OTHERS = ["c4_causal_gqa"]
 DECODE = ["d1_decode_gqa_128k", "d2_decode_mha_8k", "d3_decode_window_spec4"]
 VARLEN = ["v1_packed_causal_gqa", "l1_longformer_4k"]
+FP8_OTHERS = ["c4_causal_gqa", "c5_long_causal"]
 KERNEL_SRC = os.path.join(ROOT, "exact_tiled_attention_attn_amd", "csrc", "attn_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -225,6 +226,49 @@ def time_varlen(w, steps, warmup, torch, attn):
     return ev_ms
 
 
+def time_fp8(w, steps, warmup, torch, attn):
+    """attn_fwd_fp8 on a dense workload (inputs packed once by
+    attn_fp8_quantize, which is timed separately).  Returns (forward event
+    ms per call, quantize ms per call)."""
+    q, k, v, _ = device_inputs(w, torch)
+    q8, k8, vt8, sc = attn.fp8_quantize(q, k, v)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        st = attn.attn_fwd_fp8(q8, k8, vt8, sc, o, lse, w.B, w.Hq, w.Hkv, w.N, w.d, w.sm_scale,
+                               int(w.causal), w.window, stream)
+        if st != 0:
+            raise RuntimeError(f"attn_fwd_fp8: {attn.attn_status_string(st)}")
+
+    def quant():
+        st = attn.attn_fp8_quantize(q, k, v, q8, k8, vt8, sc, w.B, w.Hq, w.Hkv, w.N, w.d, stream)
+        if st != 0:
+            raise RuntimeError(f"attn_fp8_quantize: {attn.attn_status_string(st)}")
+
+    res = []
+    for fn in (launch, quant):
+        t_end = time.perf_counter() + 0.3
+        n = 0
+        while n < warmup or time.perf_counter() < t_end:
+            fn()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) / steps)
+    del q, k, v, q8, k8, vt8, sc, o, lse
+    return res[0], res[1]
+
+
 def cpu_baseline(w, host, seconds):
     """The float64 oracle on the host cores, on the same workload: the whole
     workload when it fits in about 2 * `seconds`, else a seeded sample of
@@ -327,6 +371,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-decode", action="store_true", help="skip the paged-decode timing")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward timing")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed-sequence / structured-mask timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -343,6 +388,7 @@ def main():
 
     from exact_tiled_attention_attn_amd import attn
     from exact_tiled_attention_attn_amd.workloads import (DECODE_WORKLOADS, MI355X_BF16_DENSE_TFLOPS,
+                                                          MI355X_FP8_DENSE_TFLOPS,
                                                           MI355X_HBM_GBPS, VARLEN_WORKLOADS,
                                                           WORKLOADS, algorithmic_bytes, bwd_flops,
                                                           decode_bytes, flops, varlen_flops)
@@ -429,6 +475,19 @@ def main():
                         "ms": round(em, 4), "flops_per_call": bf}
             torch.cuda.empty_cache()
         out["backward"] = bw
+    if not args.no_fp8:
+        f8 = {}
+        for name in [w.name] + ([] if args.no_others else FP8_OTHERS):
+            fw = WORKLOADS[name]
+            log(f"timing fp8 {name}")
+            em, qm = time_fp8(fw, args.steps, max(1, args.warmup // 2), torch, attn)
+            ff = flops(fw)
+            f8[name] = {"tflops": round(ff / (em * 1e-3) / 1e12, 2),
+                        "pct_of_fp8_peak": round(100 * ff / (em * 1e-3) / 1e12
+                                                 / MI355X_FP8_DENSE_TFLOPS, 2),
+                        "ms": round(em, 4), "quantize_ms": round(qm, 4)}
+            torch.cuda.empty_cache()
+        out["fp8"] = f8
     if not args.no_varlen:
         var = {}
         for name in VARLEN if not args.no_others else VARLEN[:1]:

@@ -7,7 +7,8 @@ does not load it; the first use of ``attn_fwd`` (or ``fwd``) does, and fails
 loudly if the library has not been built.
 """
 
-__all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "fwd_varlen", "attn_bwd", "attn_bwd_workspace_size",
+__all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "fwd_varlen", "attn_fwd_fp8",
+           "attn_fp8_quantize", "fp8_quantize", "fwd_fp8", "attn_bwd", "attn_bwd_workspace_size",
            "attn_decode_paged", "attn_decode_workspace_size", "attn_status_string", "fwd",
            "bwd", "decode", "AttnError"]
 

@@ -21,7 +21,8 @@ ATTN_ERR_UNSUPPORTED = 2
 ATTN_ERR_LAUNCH = 3
 ATTN_MAX_N = 1 << 22
 
-EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_bwd", "attn_bwd_workspace_size",
+EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_fwd_fp8", "attn_fp8_quantize",
+            "attn_fp8_vt_bytes", "attn_bwd", "attn_bwd_workspace_size",
             "attn_decode_paged", "attn_decode_workspace_size", "attn_num_variants",
             "attn_variant_name", "attn_status_string", "attn_abi_version")
 
@@ -53,6 +54,12 @@ def load_library():
     lib.attn_fwd_ex.restype = i
     lib.attn_fwd_varlen.argtypes = [vp] * 6 + [i] * 6 + [f, i, i, i, i, vp]
     lib.attn_fwd_varlen.restype = i
+    lib.attn_fp8_vt_bytes.argtypes = [i] * 4
+    lib.attn_fp8_vt_bytes.restype = ctypes.c_size_t
+    lib.attn_fp8_quantize.argtypes = [vp] * 7 + [i] * 5 + [vp]
+    lib.attn_fp8_quantize.restype = i
+    lib.attn_fwd_fp8.argtypes = [vp] * 6 + [i] * 5 + [f, i, i, vp]
+    lib.attn_fwd_fp8.restype = i
     lib.attn_bwd.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, i, vp]
     lib.attn_bwd.restype = i
     lib.attn_bwd_workspace_size.argtypes = [i, i, i]
@@ -122,6 +129,25 @@ def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, max_seqlen, total_rows, Hq, 
                                int(B), int(max_seqlen), int(total_rows), int(Hq), int(Hkv),
                                int(d), float(scale), int(causal), int(window), int(radius),
                                int(n_global), _stream(stream, q, k, v, o, lse))
+
+
+def attn_fp8_vt_bytes(B, Hkv, N, d):
+    return int(load_library().attn_fp8_vt_bytes(int(B), int(Hkv), int(N), int(d)))
+
+
+def attn_fp8_quantize(q, k, v, q8, k8, vt8, scales, B, Hq, Hkv, N, d, stream=None):
+    lib = load_library()
+    return lib.attn_fp8_quantize(_ptr(q), _ptr(k), _ptr(v), _ptr(q8), _ptr(k8), _ptr(vt8),
+                                 _ptr(scales), int(B), int(Hq), int(Hkv), int(N), int(d),
+                                 _stream(stream, q, k, v, q8, k8, vt8, scales))
+
+
+def attn_fwd_fp8(q8, k8, vt8, scales, o, lse, B, Hq, Hkv, N, d, scale, causal, window,
+                 stream=None):
+    lib = load_library()
+    return lib.attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(vt8), _ptr(scales), _ptr(o), _ptr(lse),
+                            int(B), int(Hq), int(Hkv), int(N), int(d), float(scale), int(causal),
+                            int(window), _stream(stream, q8, k8, vt8, scales, o, lse))
 
 
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, scale, causal,
@@ -332,4 +358,44 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, window=0, radius=0
                          int(bool(causal)), int(window), int(radius), int(n_global), stream)
     if st != ATTN_OK:
         raise AttnError(f"attn_fwd_varlen failed: {attn_status_string(st)} (status {st})", st)
+    return o, lse
+
+
+def fp8_quantize(q, k, v, stream=None):
+    """Pack bf16 (B, H, N, d) q, k, v for attn_fwd_fp8.  Returns
+    (q8, k8, vt8, scales) as uint8 / float32 CUDA tensors; raises on error."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.bfloat16 \
+                or not t.is_contiguous() or t.dim() != 4:
+            raise AttnError(f"{name} must be a contiguous (B, H, N, d) bf16 CUDA tensor")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    q8 = torch.empty(q.shape, dtype=torch.uint8, device=q.device)
+    k8 = torch.empty(k.shape, dtype=torch.uint8, device=q.device)
+    vt8 = torch.empty((max(attn_fp8_vt_bytes(B, Hkv, N, d), 16),), dtype=torch.uint8,
+                      device=q.device)
+    scales = torch.empty((8,), dtype=torch.float32, device=q.device)
+    st = attn_fp8_quantize(q, k, v, q8, k8, vt8, scales, B, Hq, Hkv, N, d, stream)
+    if st != ATTN_OK:
+        raise AttnError(f"attn_fp8_quantize failed: {attn_status_string(st)} (status {st})", st)
+    return q8, k8, vt8, scales
+
+
+def fwd_fp8(q8, k8, vt8, scales, causal=False, window=0, scale=None, out=None, stream=None):
+    """FP8 forward over fp8_quantize's outputs; returns (o bf16, lse fp32)."""
+    import torch
+    B, Hq, N, d = q8.shape
+    Hkv = k8.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=q8.device)
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device)
+    else:
+        o, lse = out
+    st = attn_fwd_fp8(q8, k8, vt8, scales, o, lse, B, Hq, Hkv, N, d, scale, int(bool(causal)),
+                      int(window), stream)
+    if st != ATTN_OK:
+        raise AttnError(f"attn_fwd_fp8 failed: {attn_status_string(st)} (status {st})", st)
     return o, lse

@@ -136,6 +136,44 @@ attn_status_t attn_fwd_varlen(const void *q, const void *k, const void *v, void 
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+size_t attn_fp8_vt_bytes(int B, int Hkv, int N, int d) {
+  if (B <= 0 || Hkv <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
+  const size_t np = (static_cast<size_t>(N) + 63) / 64 * 64;
+  return static_cast<size_t>(B) * static_cast<size_t>(Hkv) * static_cast<size_t>(d) * np;
+}
+
+attn_status_t attn_fp8_quantize(const void *q, const void *k, const void *v, void *q8, void *k8,
+                                void *vt8, float *scales, int B, int Hq, int Hkv, int N, int d,
+                                void *stream) {
+  const attn::FwdProblem f{q, k, v, q8, scales, B, Hq, Hkv, N, d, 1.0f, 0, 0};
+  attn_status_t st = validate(f, attn::kAuto);
+  if (st != ATTN_OK) return st;
+  if (B == 0 || N == 0) return ATTN_OK;
+  if (!k8 || !vt8) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(k8) || !aligned16(vt8)) return ATTN_ERR_UNSUPPORTED;
+  const attn::Fp8Pack p{q, k, v, q8, k8, vt8, scales, B, Hq, Hkv, N, d};
+  const hipError_t e = attn::launch_fp8_pack(p, static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidValue) return ATTN_ERR_UNSUPPORTED;
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status_t attn_fwd_fp8(const void *q8, const void *k8, const void *vt8, const float *scales,
+                           void *o, float *lse, int B, int Hq, int Hkv, int N, int d, float scale,
+                           int causal, int window, void *stream) {
+  attn::FwdProblem f{q8, k8, vt8, o, lse, B, Hq, Hkv, N, d, scale, causal, window};
+  attn_status_t st = validate(f, attn::kAuto);
+  if (st != ATTN_OK) return st;
+  if (B == 0 || N == 0) return ATTN_OK;
+  if (!scales) return ATTN_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(scales) & 3u) != 0) return ATTN_ERR_UNSUPPORTED;
+  attn::Fp8Problem p{q8, k8, vt8, scales, o, lse, B, Hq, Hkv, N, d, scale, causal, window};
+  if (p.window >= N) p.window = 0;
+  if (p.window < 0) p.window = 0;
+  const hipError_t e = attn::launch_fwd_fp8(p, static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidValue) return ATTN_ERR_UNSUPPORTED;
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 size_t attn_bwd_workspace_size(int B, int Hq, int N) {
   if (B <= 0 || Hq <= 0 || N <= 0) return 0;
   return static_cast<size_t>(B) * static_cast<size_t>(Hq) * static_cast<size_t>(N) * sizeof(float);

@@ -62,6 +62,28 @@ struct BwdProblem {
 // Enqueue the three backward kernels (Delta, dQ, dK/dV) for `p` on `stream`.
 hipError_t launch_bwd(const BwdProblem &p, hipStream_t stream);
 
+// FP8 packing: bf16 q, k, v -> e4m3 q8, k8 and the permuted transpose vt8,
+// scales[0..2] (and the amax values in scales[3..5]).
+struct Fp8Pack {
+  const void *q, *k, *v;
+  void *q8, *k8, *vt8;
+  float *scales;
+  int B, Hq, Hkv, N, d;
+};
+hipError_t launch_fp8_pack(const Fp8Pack &p, hipStream_t stream);
+
+// FP8 forward over packed inputs.
+struct Fp8Problem {
+  const void *q8, *k8, *vt8;
+  const float *scales;
+  void *o;
+  float *lse;
+  int B, Hq, Hkv, N, d;
+  float scale;
+  int causal, window;
+};
+hipError_t launch_fwd_fp8(const Fp8Problem &p, hipStream_t stream);
+
 // One paged decode problem, already validated by the entry point.
 struct DecodeProblem {
   const void *q, *k_cache, *v_cache;

@@ -24,6 +24,7 @@ from dataclasses import dataclass, field
 
 MI355X_BF16_DENSE_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 bf16 FLOP/CU/clk
 MI355X_HBM_GBPS = 8000.0
+MI355X_FP8_DENSE_TFLOPS = 5033.2  # twice the bf16 rate
 
 
 @dataclass(frozen=True)

@@ -132,6 +132,37 @@ attn_status_t attn_fwd_varlen(const void *q, const void *k, const void *v, void 
                               int Hq, int Hkv, int d, float scale, int causal, int window,
                               int radius, int n_global, void *stream);
 
+/* FP8 forward.  "Efficient attention: long context and sub-quadratic
+ * variants" (section "FlashAttention: exact attention, IO-aware") attaches
+ * an FP8 path to FlashAttention-3.  Format: OCP FP8 E4M3 (bias 7, largest
+ * finite 448, NaN = 0x7F / 0xFF, round to nearest even).  One power-of-two
+ * scale per tensor: s = 2^e with e the smallest integer such that
+ * max|x| <= 448 * 2^e, code = e4m3(x / s), value = code * s.
+ *
+ * attn_fp8_quantize: bf16 q, k, v (attn_fwd's layouts) ->
+ *   q8   e4m3 [B][Hq][N][d]
+ *   k8   e4m3 [B][Hkv][N][d]
+ *   vt8  e4m3 [B][Hkv][d][Np], Np = N rounded up to a multiple of 64: V
+ *        transposed, and within each 64-key block position p holds key
+ *        32 (b / 16) + 8 ((b % 16) / 4) + 4 h + b % 4 with h = p / 32,
+ *        b = p % 32 (the order the kernel's P^T operand holds the keys);
+ *        positions of keys >= N hold 0.  attn_fp8_vt_bytes gives its size.
+ *   scales  device float[6], written: scales[0..2] = s_q, s_k, s_v;
+ *        scales[3..5] hold the amax values.
+ * All pointers 16-byte aligned (scales 4-byte).  Four kernels on `stream`.
+ *
+ * attn_fwd_fp8: the attention of the dequantised tensors, with attn_fwd's
+ * arguments otherwise (o bf16, lse fp32, causal, window, GQA).  Inside,
+ * the weights P are rounded to e4m3 (scaled by 2^8, exact running max) for
+ * the P V product; S and O accumulate in fp32. */
+size_t attn_fp8_vt_bytes(int B, int Hkv, int N, int d);
+attn_status_t attn_fp8_quantize(const void *q, const void *k, const void *v, void *q8, void *k8,
+                                void *vt8, float *scales, int B, int Hq, int Hkv, int N, int d,
+                                void *stream);
+attn_status_t attn_fwd_fp8(const void *q8, const void *k8, const void *vt8, const float *scales,
+                           void *o, float *lse, int B, int Hq, int Hkv, int N, int d, float scale,
+                           int causal, int window, void *stream);
+
 /* Backward pass: the gradients of a loss L with respect to q, k and v, given
  * dout = dL/do for the forward above.  "Efficient attention: long context
  * and sub-quadratic variants" (section "Against the real libraries") pairs
@@ -233,7 +264,7 @@ const char *attn_variant_name(int variant);
 const char *attn_status_string(attn_status_t status);
 
 /* ABI version of this header (incremented on any signature change). */
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 int attn_abi_version(void);
 
 #ifdef __cplusplus
