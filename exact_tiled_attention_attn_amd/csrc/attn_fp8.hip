@@ -18,9 +18,11 @@
 // 8 waves x 32 query rows, 64-key tiles double-buffered through LDS, one
 // query per lane), with v_mfma_scale_f32_32x32x64_f8f6f4: S^T = K Q^T takes
 // D / 64 products per 32 keys and O^T += V^T P^T one product per 32 d
-// values.  The weights are P' = 2^8 exp2(c s - m) with the exact running
-// max m, so P' <= 256 fits e4m3 and weights down to 2^-14 of the row max
-// keep normal e4m3 precision; P' is rounded to e4m3 (RNE) for the product.
+// values.  The weights are P' = 2^4 exp2(c s - m) against a lazily moved
+// reference max m (it moves when a row's tile max exceeds it by more than 4
+// log2 units, and only then is O rescaled), so P' <= 256 fits e4m3 and
+// weights down to 2^-10 of the reference keep normal e4m3 precision; P' is
+// rounded to e4m3 (RNE) for the product.
 // The descales s_q s_k enter the exponent factor c, s_v the epilogue.
 
 #include <hip/hip_runtime.h>
@@ -42,7 +44,12 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i32x4 lds_i32x4_t;
 
 constexpr int kBN8 = 64;          // keys per tile
-constexpr float kPShift = 8.0f;   // log2 of the weight scaling before e4m3
+// Weights P' = 2^kPShift exp2(c s - m) against a reference max m that
+// moves only when a row's tile max exceeds it by more than kTau8 (log2
+// units), so P' <= 2^(kPShift + kTau8) = 256 <= 448 fits e4m3, and weights
+// down to 2^-(6 + kPShift) of the reference keep normal e4m3 precision.
+constexpr float kPShift = 4.0f;
+constexpr float kTau8 = 4.0f;
 
 // Key (0..63) of a 64-key tile held at byte b (0..31) of lane half h of the
 // P^T operand: the S^T accumulators of key block rb = b / 16 hold, in
@@ -304,10 +311,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(F8Params prm) 
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rb][r]);
     }
     const float mt = wave_max_pair(mx) * c;
-    const bool move = __builtin_amdgcn_ballot_w64(mt > m2) != 0;
-    const float mnew = fmaxf(m2, mt);
+    const bool move = __builtin_amdgcn_ballot_w64(mt > m2 + kTau8) != 0;
+    const float mnew = move ? fmaxf(m2, mt) : m2;
     const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
     m2 = mnew;
+    if (move) {
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < g::kDB; ++db) oacc[db] *= alpha;
+    }
     const float off = kPShift - mnew;
     float part = 0.0f;
     int pw[8];
@@ -323,11 +335,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(F8Params prm) 
       const int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
       pw[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], x, true);
     }
-    lsum = lsum * alpha + part;
+    lsum += part;
     const i32x8 pf = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
 #pragma unroll
     for (int db = 0; db < g::kDB; ++db) {
-      if (move) oacc[db] *= alpha;
       const lchar *p = set + g::kKTile + v_lane + db * 32 * g::kVStride;
       const i32x4 a = *(const lds_i32x4_t *)p, b = *(const lds_i32x4_t *)(p + 16);
       const i32x8 vf = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
