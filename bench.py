@@ -21,6 +21,7 @@ score, and the FP8 forward (attn_fwd_fp8) against the dense fp8 peak.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -69,6 +70,43 @@ def device_inputs(w, torch):
     return q.to(dev), k.to(dev), v.to(dev), (q, k, v)
 
 
+def run_timed(launch, steps, warmup, seconds, torch, stream, sync_every=8):
+    """Warm up (at least `warmup` calls and at least `seconds` of them: the
+    clock ramps up over the first milliseconds of sustained load), then time
+    `steps` back-to-back calls between two events on `stream`.
+
+    The region is bracketed by synchronisations, and nothing stands between
+    the first synchronisation and the first timed launch but the start
+    event: after even a few milliseconds of idling the GPU runs the next
+    tens of calls measurably slower.  So Python's cyclic garbage collector
+    is off from the start of the warmup to the end (a collection there would
+    idle the GPU, and the events would count that time as well).  Returns
+    (event ms per call, host wall ms per call)."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    gc.collect()
+    gc.disable()
+    try:
+        t_end = time.perf_counter() + seconds
+        n = 0
+        while n < warmup or time.perf_counter() < t_end:
+            launch()
+            n += 1
+            if n % sync_every == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    finally:
+        gc.enable()
+    return e0.elapsed_time(e1) / steps, wall_ms
+
+
 def time_workload(w, steps, warmup, variant, torch, attn):
     """Returns (wall ms/step, event ms/launch, host tensors)."""
     q, k, v, host = device_inputs(w, torch)
@@ -82,26 +120,7 @@ def time_workload(w, steps, warmup, variant, torch, attn):
         if st != 0:
             raise RuntimeError(f"attn_fwd_ex: {attn.attn_status_string(st)}")
 
-    # at least `warmup` launches and at least 0.5 s of them: the clock ramps
-    # up over the first milliseconds of sustained MFMA load
-    t_end = time.perf_counter() + 0.5
-    n = 0
-    while n < warmup or time.perf_counter() < t_end:
-        launch()
-        n += 1
-        if n % 8 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(steps):
-        launch()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    ev_ms = e0.elapsed_time(e1) / steps
+    ev_ms, wall_ms = run_timed(launch, steps, warmup, 0.5, torch, stream)
     del q, k, v, o, lse
     return wall_ms, ev_ms, host
 
@@ -124,22 +143,7 @@ def time_backward(w, steps, warmup, torch, attn):
         if st != 0:
             raise RuntimeError(f"attn_bwd: {attn.attn_status_string(st)}")
 
-    t_end = time.perf_counter() + 0.5
-    n = 0
-    while n < warmup or time.perf_counter() < t_end:
-        launch()
-        n += 1
-        if n % 4 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        launch()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ev_ms = e0.elapsed_time(e1) / steps
+    ev_ms, _ = run_timed(launch, steps, warmup, 0.5, torch, stream, sync_every=4)
     del q, k, v, do, o, lse, dq, dk, dv, ws
     return ev_ms
 
@@ -168,22 +172,7 @@ def time_decode(w, steps, warmup, torch, attn):
         if st != 0:
             raise RuntimeError(f"attn_decode_paged: {attn.attn_status_string(st)}")
 
-    t_end = time.perf_counter() + 0.3
-    n = 0
-    while n < warmup or time.perf_counter() < t_end:
-        launch()
-        n += 1
-        if n % 8 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        launch()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ev_ms = e0.elapsed_time(e1) / steps
+    ev_ms, _ = run_timed(launch, steps, warmup, 0.3, torch, stream)
     del q, kc, vc, table, lt, o, lse, ws
     return ev_ms, lens
 
@@ -206,22 +195,7 @@ def time_varlen(w, steps, warmup, torch, attn):
         if st != 0:
             raise RuntimeError(f"attn_fwd_varlen: {attn.attn_status_string(st)}")
 
-    t_end = time.perf_counter() + 0.3
-    n = 0
-    while n < warmup or time.perf_counter() < t_end:
-        launch()
-        n += 1
-        if n % 8 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        launch()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ev_ms = e0.elapsed_time(e1) / steps
+    ev_ms, _ = run_timed(launch, steps, warmup, 0.3, torch, stream)
     del q, k, v, cu, o, lse
     return ev_ms
 
@@ -247,26 +221,10 @@ def time_fp8(w, steps, warmup, torch, attn):
         if st != 0:
             raise RuntimeError(f"attn_fp8_quantize: {attn.attn_status_string(st)}")
 
-    res = []
-    for fn in (launch, quant):
-        t_end = time.perf_counter() + 0.3
-        n = 0
-        while n < warmup or time.perf_counter() < t_end:
-            fn()
-            n += 1
-            if n % 8 == 0:
-                torch.cuda.synchronize()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        res.append(e0.elapsed_time(e1) / steps)
+    em, _ = run_timed(launch, steps, warmup, 0.3, torch, stream)
+    qm, _ = run_timed(quant, steps, warmup, 0.3, torch, stream)
     del q, k, v, q8, k8, vt8, sc, o, lse
-    return res[0], res[1]
+    return em, qm
 
 
 def cpu_baseline(w, host, seconds):

@@ -86,22 +86,40 @@ __global__ void attn_fp8_clear_kernel(float *scales) {
   if (threadIdx.x < 6) scales[threadIdx.x] = 0.0f;
 }
 
-// amax of tensor blockIdx.y, 8 values per thread per step
+// amax of tensor blockIdx.y: four independent 16-byte loads per thread per
+// step keep enough reads in flight to run near the HBM rate
 __global__ __launch_bounds__(256) void attn_fp8_amax_kernel(PackParams pp) {
   const int t = blockIdx.y;
-  const uint16_t *x = pp.x[t];
+  const bf16x8 *x = reinterpret_cast<const bf16x8 *>(pp.x[t]);
   const long long n8 = pp.n[t] / 8;
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   float m = 0.0f;
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
-       i += (long long)gridDim.x * blockDim.x) {
-    const bf16x8 v = *(const bf16x8 *)(x + 8 * i);
+  for (; i + 3 * stride < n8; i += 4 * stride) {
+    bf16x8 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = x[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)v[u][e]));
+  }
+  for (; i < n8; i += stride) {
+    const bf16x8 v = x[i];
 #pragma unroll
     for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)v[e]));
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((threadIdx.x & 63) == 0)
+  // one atomic per workgroup: atomics on one address serialise, and every
+  // workgroup reaches this point at about the same time
+  __shared__ float wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     atomicMax(reinterpret_cast<unsigned *>(pp.scales + 3 + t), __float_as_uint(m));
+  }
 }
 
 // Q and K codes: 8 values per thread per step; block (0, 0) also publishes
@@ -422,7 +440,7 @@ hipError_t launch_pack_d(const Fp8Pack &p, hipStream_t stream) {
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&attn_fp8_clear_kernel), dim3(1),
                                  dim3(64), clear_args, 0, stream);
   if (e != hipSuccess) return e;
-  e = hipLaunchKernel(reinterpret_cast<const void *>(&attn_fp8_amax_kernel), dim3(1024, 3),
+  e = hipLaunchKernel(reinterpret_cast<const void *>(&attn_fp8_amax_kernel), dim3(512, 3),
                       dim3(256), args, 0, stream);
   if (e != hipSuccess) return e;
   e = hipLaunchKernel(reinterpret_cast<const void *>(&attn_fp8_pack_qk_kernel), dim3(2048, 2),
