@@ -95,6 +95,7 @@ struct Params {
   int total_rows;
   int radius;
   int nglob;
+  int compact;    // sequence lengths differ: launch only non-empty tiles first
 };
 
 template <int D>
@@ -224,6 +225,70 @@ struct Task {
   bool empty;          // no row of the workgroup lies inside its sequence
 };
 
+// Sum over the wave, returned as a scalar (so everything derived from it
+// stays in scalar registers).
+__device__ __forceinline__ int wave_sum_int(int x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+// Packed sequences of different lengths leave many (rank, sequence) slots
+// of the rank-major order empty: a short sequence has no tile at the high
+// ranks.  Scattered through the launch order, such workgroups cost almost
+// as much as short real ones.  Compacted order: workgroup n takes the n-th
+// non-empty (rank, sequence, head group) in the same rank-major order, so
+// the empty ones all come last.  S(r) = number of non-empty (rank, sequence)
+// slots below rank r; workgroup n serves slot m = n / groups at the largest
+// r with S(r) <= m.  Each wave computes it with its lanes over the
+// sequences (all wave-uniform results).  Returns false past the last slot.
+template <int kRows>
+__device__ __forceinline__ bool compact_slot(const Params &prm, int n, int &rank, int &b_out,
+                                             int &hg) {
+  const int lane = threadIdx.x & 63;
+  const int nq = prm.nq;
+  auto tiles_of = [&](int b) {  // row tiles of sequence b (0 past the end)
+    if (b >= prm.B) return 0;
+    const int s0 = min(max(prm.cu[b], 0), prm.total_rows);
+    const int s1 = min(max(prm.cu[b + 1], 0), prm.total_rows);
+    return min((max(s1 - s0, 0) + kRows - 1) / kRows, nq);  // rows past nq * kRows: no tile
+  };
+  // slots of one sequence below rank r: causal ranks run heaviest (last)
+  // row tile first, so sequence b first appears at rank nq - nt
+  auto below = [&](int nt, int r) { return prm.causal ? max(0, r - (nq - nt)) : min(r, nt); };
+  const int nt0 = tiles_of(lane);
+  const int nchunks = (prm.B + 63) / 64;
+  auto S = [&](int r) {
+    int acc = below(nt0, r);
+    for (int c = 1; c < nchunks; ++c) acc += below(tiles_of(64 * c + lane), r);
+    return wave_sum_int(acc);
+  };
+  const int m = n / prm.groups;
+  hg = n % prm.groups;
+  int lo = 0, hi = nq;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (S(mid) <= m) lo = mid; else hi = mid - 1;
+  }
+  if (lo >= nq) return false;
+  rank = lo;
+  const int qi = prm.causal ? nq - 1 - lo : lo;
+  int jb = m - S(lo);  // the jb-th sequence (in batch order) with a tile at this rank
+  for (int c = 0; c < nchunks; ++c) {
+    const int nt = c == 0 ? nt0 : tiles_of(64 * c + lane);
+    const unsigned long long has = __builtin_amdgcn_ballot_w64(qi < nt);
+    const int cnt = __popcll(has);
+    if (jb < cnt) {
+      const int before = __popcll(has & ((1ull << lane) - 1ull));
+      const unsigned long long pick = __builtin_amdgcn_ballot_w64(qi < nt && before == jb);
+      b_out = 64 * c + __ffsll((long long)pick) - 1;
+      return true;
+    }
+    jb -= cnt;
+  }
+  return false;
+}
+
 // kRows query rows per workgroup, P heads per workgroup (wave w serves head
 // w % P on rows (w / P) * 32 ..).  GEN: packed sequences [cu[b], cu[b+1]).
 template <int P, int kRows, bool GEN>
@@ -234,9 +299,18 @@ __device__ __forceinline__ Task make_task(const Params &prm, int wave) {
     // packed sequences of different lengths: tile rank slowest, so the
     // heaviest tiles of every sequence go first and consecutive workgroups
     // (dealt round-robin to the XCDs) spread every sequence over all XCDs
-    const int nbh = prm.B * prm.groups;
-    qrank = blockIdx.x / nbh;
-    hgb = blockIdx.x % nbh;
+    if (prm.compact) {
+      int b, hg;
+      if (!compact_slot<kRows>(prm, blockIdx.x, qrank, b, hg)) {
+        tk.empty = true;
+        return tk;
+      }
+      hgb = b * prm.groups + hg;
+    } else {
+      const int nbh = prm.B * prm.groups;
+      qrank = blockIdx.x / nbh;
+      hgb = blockIdx.x % nbh;
+    }
   } else {
     const int logical = xcd_remap(blockIdx.x, prm.total);
     qrank = logical % prm.nq;
@@ -686,6 +760,7 @@ hipError_t launch_gen_t(const VarlenProblem &p, hipStream_t stream) {
   prm.total_rows = p.total_rows;
   prm.radius = p.radius;
   prm.nglob = p.n_global;
+  prm.compact = (long long)p.B * p.max_seqlen != p.total_rows;
   void *args[] = {&prm};
   return hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_kernel<D, NW, P, true>),
                          dim3(prm.total), dim3(NW * 64), args, 0, stream);

@@ -68,13 +68,25 @@ CASES = [
     ([777, 33], 8, 2, 128, False, 0, 0, 64),            # globals, no band: full rows
     ([2048, 5, 1500], 16, 2, 128, False, 0, 256, 16),   # Longformer-like
     ([4096], 4, 4, 64, False, 0, 256, 300),             # more globals than a tile
+    # more than 64 sequences of different lengths: the compacted launch
+    # order scans the lengths in chunks of 64 per wave
+    ([int(x) for x in np.random.default_rng(7).integers(0, 300, size=150)],
+     4, 2, 64, True, 0, 0, 0),
+    ([int(x) for x in np.random.default_rng(8).integers(1, 200, size=70)],
+     8, 8, 128, False, 0, 30, 2),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
+def case_id(c):
+    lens = c[0]
+    short = str(lens) if len(lens) <= 8 else f"[{len(lens)} lengths, total {sum(lens)}]"
+    return str((short,) + tuple(c[1:]))
+
+
+@pytest.mark.parametrize("case", CASES, ids=[case_id(c) for c in CASES])
 def test_varlen_parity(case):
     lens, Hq, Hkv, d, causal, window, radius, n_global = case
-    say(f"case varlen {case}")
+    say(f"case varlen {case_id(case)}")
     q, k, v, cu = make_packed_qkv(lens, Hq, Hkv, d, seed=300 + len(lens) + Hq)
     o, lse = run(q, k, v, cu, causal, window, radius, n_global)
     o_ref, l_ref = attention_general(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(d),
