@@ -259,3 +259,75 @@ def test_varlen_empty_problem_is_ok_and_launches_nothing(lib, kw):
     a = dict(VAR_GOOD)
     a.update(kw)
     assert attn.attn_fwd_varlen(**a) == attn.ATTN_OK
+
+
+FP8Q_GOOD = dict(q=P, k=P, v=P, q8=P, k8=P, vt8=P, scales=P, B=1, Hq=4, Hkv=2, N=64, d=128)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(v=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(q8=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(k8=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(vt8=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scales=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(B=-1), attn.ATTN_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_INVALID_ARG),
+    (dict(d=32), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(k8=P + 2), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(vt8=P + 8), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(N=(1 << 22) + 1), attn.ATTN_ERR_UNSUPPORTED),
+])
+def test_fp8_quantize_rejects_bad_arguments_without_launching(lib, kw, expect):
+    a = dict(FP8Q_GOOD)
+    a.update(kw)
+    assert attn.attn_fp8_quantize(**a) == expect
+
+
+FP8F_GOOD = dict(q8=P, k8=P, vt8=P, scales=P, o=P, lse=P, B=1, Hq=4, Hkv=2, N=64, d=128,
+                 scale=0.1, causal=1, window=0)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q8=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(vt8=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scales=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(o=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(lse=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_INVALID_ARG),
+    (dict(causal=2), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), attn.ATTN_ERR_INVALID_ARG),
+    (dict(d=96), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(causal=0, window=8), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(scales=P + 2), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(N=(1 << 22) + 1), attn.ATTN_ERR_UNSUPPORTED),
+])
+def test_fwd_fp8_rejects_bad_arguments_without_launching(lib, kw, expect):
+    a = dict(FP8F_GOOD)
+    a.update(kw)
+    assert attn.attn_fwd_fp8(**a) == expect
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=0),
+                                dict(N=0, q8=0, k8=0, vt8=0, scales=0, o=0, lse=0)])
+def test_fwd_fp8_empty_problem_is_ok_and_launches_nothing(lib, kw):
+    a = dict(FP8F_GOOD)
+    a.update(kw)
+    assert attn.attn_fwd_fp8(**a) == attn.ATTN_OK
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=0),
+                                dict(B=0, q=0, k=0, v=0, q8=0, k8=0, vt8=0, scales=0)])
+def test_fp8_quantize_empty_problem_is_ok_and_launches_nothing(lib, kw):
+    a = dict(FP8Q_GOOD)
+    a.update(kw)
+    assert attn.attn_fp8_quantize(**a) == attn.ATTN_OK
+
+
+def test_fp8_vt_bytes(lib):
+    # V^T codes: d rows of the key count rounded up to 64, per (batch, KV head)
+    assert attn.attn_fp8_vt_bytes(2, 8, 100, 128) == 2 * 8 * 128 * 128
+    assert attn.attn_fp8_vt_bytes(1, 1, 64, 64) == 64 * 64
+    assert attn.attn_fp8_vt_bytes(1, 1, 65, 64) == 64 * 128
+    assert attn.attn_fp8_vt_bytes(0, 1, 64, 64) == 0
+    assert attn.attn_fp8_vt_bytes(1, 1, 64, 96) == 0
