@@ -153,8 +153,10 @@ attn_status_t attn_fwd_varlen(const void *q, const void *k, const void *v, void 
  *
  * attn_fwd_fp8: the attention of the dequantised tensors, with attn_fwd's
  * arguments otherwise (o bf16, lse fp32, causal, window, GQA).  Inside,
- * the weights P are rounded to e4m3 (scaled by 2^8, exact running max) for
- * the P V product; S and O accumulate in fp32. */
+ * the weights are rounded to e4m3 for the P V product as 2^4 exp(s - m) with
+ * a reference max m that moves only when a row's max exceeds it by more
+ * than 4 log2 units (so they stay <= 2^8 < 448); S and O accumulate in
+ * fp32, lse sums the unrounded weights. */
 size_t attn_fp8_vt_bytes(int B, int Hkv, int N, int d);
 attn_status_t attn_fp8_quantize(const void *q, const void *k, const void *v, void *q8, void *k8,
                                 void *vt8, float *scales, int B, int Hq, int Hkv, int N, int d,
