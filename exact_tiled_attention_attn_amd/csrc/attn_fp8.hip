@@ -321,7 +321,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(F8Params prm) 
         }
       }
     }
-    // exact running max (scaled log2 units), weights scaled by 2^kPShift
+    // tile max (scaled log2 units); the reference max moves lazily (kTau8)
     float mx = s[0][0];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
