@@ -311,3 +311,19 @@ def test_workload_parity_every_row(name, variant):
         o_ref, l_ref = attention_forward(qf, kf, vf, w.sm_scale, w.causal, w.window,
                                          workers=16)
     check(o, lse, o_ref, l_ref, f"{name} (every row) v{variant}")
+
+
+@pytest.mark.parametrize("window", [0, 4096])
+def test_longest_sequence(window):
+    """N = ATTN_MAX_N (2^22), d = 128: the largest slice the 32-bit buffer
+    offsets address.  Checked on sampled rows, the last one included."""
+    N, d = attn.ATTN_MAX_N, 128
+    say(f"case longest sequence N={N} window={window}")
+    q, k, v = make_qkv(1, 1, 1, N, d, seed=77)
+    o, lse = run(q, k, v, True, window)
+    rows = sample_rows(N, 12, seed=78, edges=(0, 63, 64, N // 2, N - 65, N - 64, N - 1))
+    say("  HIP done; oracle on the sampled rows")
+    o_ref, l_ref = attention_rows(q.float().numpy(), k.float().numpy(), v.float().numpy(),
+                                  1 / math.sqrt(d), True, window, rows=rows)
+    idx = torch.from_numpy(rows)
+    check(o[0, 0, idx], lse[0, 0, idx], o_ref[0, 0], l_ref[0, 0], f"N={N} window={window}")
