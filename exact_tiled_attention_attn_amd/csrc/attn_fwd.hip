@@ -588,7 +588,7 @@ __device__ __forceinline__ void write_out(const Params &prm, const Task &tk, int
 // between two workgroup barriers.
 // ---------------------------------------------------------------------------
 template <int D, int NW, int P, bool GEN>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params prm) {
+__global__ __launch_bounds__(NW * 64, (NW == 4 && D == 64) ? 3 : 2) void attn_fwd_kernel(Params prm) {
   using g = Geo<D>;
   constexpr int kRows = 32 * NW / P;  // query rows per workgroup
 
@@ -733,9 +733,16 @@ hipError_t launch_t(const FwdProblem &p, hipStream_t stream) {
                          dim3(prm.total), dim3(NW * 64), args, 0, stream);
 }
 
+// Waves per workgroup of the general (packed, structured-mask) kernels:
+// at d = 64 three 4-wave workgroups share a CU (138 VGPRs, 43 KB of LDS),
+// and their waves, not held together by one barrier, overlap one another's
+// softmax and matrix products; at d = 128 one 8-wave workgroup per CU.
+template <int D>
+constexpr int kGenWaves = D == 64 ? 4 : 8;
+
 template <int D, int P>
 hipError_t launch_gen_t(const VarlenProblem &p, hipStream_t stream) {
-  constexpr int NW = 8;
+  constexpr int NW = kGenWaves<D>;
   constexpr int kRows = 32 * NW / P;
   Params prm{};
   prm.q = static_cast<const uint16_t *>(p.q);
@@ -769,7 +776,7 @@ hipError_t launch_gen_t(const VarlenProblem &p, hipStream_t stream) {
 template <int D>
 hipError_t launch_gen_d(const VarlenProblem &p, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
-  if (G % 8 == 0) return launch_gen_t<D, 8>(p, stream);
+  if (kGenWaves<D> >= 8 && G % 8 == 0) return launch_gen_t<D, (kGenWaves<D> >= 8 ? 8 : 4)>(p, stream);
   if (G % 4 == 0) return launch_gen_t<D, 4>(p, stream);
   if (G % 2 == 0) return launch_gen_t<D, 2>(p, stream);
   return launch_gen_t<D, 1>(p, stream);
@@ -802,7 +809,9 @@ const char *variant_name(int variant) {
 }
 
 hipError_t launch_fwd(const FwdProblem &p, int variant, hipStream_t stream) {
-  const int v = variant == kAuto ? kWaves8 : variant;
+  // default: 8 waves at d = 128 (one workgroup per CU); 4 waves at d = 64,
+  // where 138 VGPRs let three 4-wave workgroups share a CU
+  const int v = variant != kAuto ? variant : p.d == 64 ? kWaves4 : kWaves8;
   return p.d == 128 ? launch_d<128>(p, v, stream) : launch_d<64>(p, v, stream);
 }
 
