@@ -43,7 +43,10 @@
 // Schedule: per key tile, every wave runs S, softmax and PV between two
 // workgroup barriers; the two waves that share a SIMD (8-wave variant) run
 // their softmax together, which is what keeps the vector ALU busy: one wave
-// alone issues a vector instruction only every few clocks.
+// alone issues a vector instruction only every few clocks.  At d = 64 the
+// default is the 4-wave variant: it fits three workgroups per CU, whose
+// waves (held together by no barrier) overlap one another's softmax and
+// matrix products.
 
 #include <hip/hip_runtime.h>
 
@@ -776,7 +779,9 @@ hipError_t launch_gen_t(const VarlenProblem &p, hipStream_t stream) {
 template <int D>
 hipError_t launch_gen_d(const VarlenProblem &p, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
-  if (kGenWaves<D> >= 8 && G % 8 == 0) return launch_gen_t<D, (kGenWaves<D> >= 8 ? 8 : 4)>(p, stream);
+  if constexpr (kGenWaves<D> >= 8) {
+    if (G % 8 == 0) return launch_gen_t<D, 8>(p, stream);
+  }
   if (G % 4 == 0) return launch_gen_t<D, 4>(p, stream);
   if (G % 2 == 0) return launch_gen_t<D, 2>(p, stream);
   return launch_gen_t<D, 1>(p, stream);
@@ -786,7 +791,9 @@ template <int D, int NW>
 hipError_t launch_nw(const FwdProblem &p, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
   // heads packed per workgroup: the largest power of two <= NW dividing G
-  if (NW >= 8 && G % 8 == 0) return launch_t<D, NW, (NW >= 8 ? 8 : 1)>(p, stream);
+  if constexpr (NW >= 8) {
+    if (G % 8 == 0) return launch_t<D, NW, 8>(p, stream);
+  }
   if (G % 4 == 0) return launch_t<D, NW, 4>(p, stream);
   if (G % 2 == 0) return launch_t<D, NW, 2>(p, stream);
   return launch_t<D, NW, 1>(p, stream);
