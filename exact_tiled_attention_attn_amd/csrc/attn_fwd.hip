@@ -30,8 +30,10 @@
 // * K and V tiles go HBM -> registers -> LDS, 16 bytes per lane per load.
 //   The loads of a later tile are issued a whole tile of MFMAs before their
 //   LDS stores.  (Direct buffer_load ... lds would save the registers, but
-//   the compiler then waits for every outstanding vector load before each
-//   transposed LDS read.)  The buffer descriptor spans one (batch, KV-head)
+//   into one LDS array the compiler waits for every outstanding vector load
+//   before each LDS read; with one array per buffer it does not, yet a
+//   wave's direct load fills 64 consecutive 16-byte slots, which the padded
+//   rows below do not form.)  The buffer descriptor spans one (batch, KV-head)
 //   slice, so keys past N read as zero.  LDS rows are padded so both the
 //   b128 K reads and the transposed V reads hit distinct banks.
 // * GQA: the query heads sharing a KV head are packed into one workgroup
