@@ -28,8 +28,8 @@
 //   of 4 consecutive d values of key row j and lane i receives the 4 keys of
 //   column i.
 // * K and V tiles go HBM -> registers -> LDS, 16 bytes per lane per load.
-//   The loads of a later tile are issued a whole tile of MFMAs before their
-//   LDS stores.  (Direct buffer_load ... lds would save the registers, but
+//   Two register stages keep the next two tiles in flight, so a tile's loads
+//   are issued two tiles of MFMAs before their LDS stores.  (Direct buffer_load ... lds would save the registers, but
 //   into one LDS array the compiler waits for every outstanding vector load
 //   before each LDS read; with one array per buffer it does not, yet a
 //   wave's direct load fills 64 consecutive 16-byte slots, which the padded
@@ -624,13 +624,23 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D == 64) ? 3 : 2) void attn_fw
   RowState st;
   const float c = prm.c;
 
-  TileStage<D, NW> stage;
+  // Q is settled in registers before any tile load is issued, so that no
+  // later use of Q waits for the tile loads in flight.
+#pragma unroll
+  for (int kk = 0; kk < g::kKSteps; ++kk) asm volatile("" : "+v"(qf[kk]) : : "memory");
+
+  // Two register stages: tiles k + 1 and k + 2 are in flight while tile k
+  // is computed, so each tile's loads have two tiles of compute to land.
+  // Every step issues its loads, past the last tile at row N (outside the
+  // buffer range: no memory access, zeros), so the number of loads in
+  // flight is the same on every path and each store waits only for its own.
   const int count = tk.wg.count();
-  if (count > 0) {
-    const int t0 = tk.wg.tile(0);
-    stage.load(rs_k, rs_v, t0 * kBN, t0 * kBN, tid);
-    stage.store(set0, set0 + g::kKTileB, tid);
-  }
+  auto row_of = [&](int k) { return k < count ? tk.wg.tile(k) * kBN : N; };
+  TileStage<D, NW> stage0, stage1;
+  stage0.load(rs_k, rs_v, row_of(0), row_of(0), tid);
+  if (count > 0) stage0.store(set0, set0 + g::kKTileB, tid);
+  stage1.load(rs_k, rs_v, row_of(1), row_of(1), tid);
+  stage0.load(rs_k, rs_v, row_of(2), row_of(2), tid);
   __syncthreads();
 
   // S^T, mask, online softmax and O^T update for key tile t held in `set`.
@@ -687,26 +697,28 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D == 64) ? 3 : 2) void attn_fw
     }
   };
 
-  // One key tile: start loading the next tile into registers, compute this
-  // one from LDS (if this wave sees any of its keys), then park the next tile
-  // in the other buffer set.  The register loads are only waited for at that
-  // final store, so they overlap the whole tile's compute.
-  auto step = [&](const int k, lchar *const cur_set, lchar *const next_set) {
-    const bool more = k + 1 < count;
-    if (more) {
-      const int tn = tk.wg.tile(k + 1);
-      stage.load(rs_k, rs_v, tn * kBN, tn * kBN, tid);
-    }
+  // One key tile: compute it from LDS (if this wave sees any of its keys),
+  // park tile k + 1 (loaded two steps earlier) in the other buffer set, and
+  // start loading tile k + 3 into the registers that held it.
+  auto step = [&](const int k, lchar *const cur_set, lchar *const next_set,
+                  TileStage<D, NW> &nxt) {
     const int t = tk.wg.tile(k);
     if (tk.w.has(t)) compute(t, cur_set);
-    if (more) stage.store(next_set, next_set + g::kKTileB, tid);
+    if (k + 1 < count) nxt.store(next_set, next_set + g::kKTileB, tid);
+    nxt.load(rs_k, rs_v, row_of(k + 3), row_of(k + 3), tid);
     __syncthreads();
   };
 
-  for (int k = 0; k < count; k += 2) {
-    step(k, set0, set1);
-    if (k + 1 < count) step(k + 1, set1, set0);
+  // Pairs of steps with no exit between them, so the loads in flight at
+  // the loop head are always stage1's then stage0's; an odd last tile runs
+  // after the loop.
+  int k = 0;
+  for (; k + 1 < count; k += 2) {
+    step(k, set0, set1, stage1);
+    step(k + 1, set1, set0, stage0);
   }
+  if (k < count) step(k, set0, set1, stage1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load left in flight
 
   write_out<D>(prm, tk, l32, hh, oacc, st);
 }
