@@ -56,27 +56,31 @@
 #include <cmath>
 #include <cstdint>
 
+#include "attn_device.h"
 #include "attn_internal.h"
 
 namespace attn {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((vector_size(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
-typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
-typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
-typedef char __attribute__((address_space(3))) lchar;
+using dev::bf16x2;
+using dev::bf16x4;
+using dev::bf16x8;
+using dev::f32x16;
+using dev::i16x4;
+using dev::kLn2;
+using dev::kLog2e;
+using dev::lchar;
+using dev::lds_bf16x8_t;
+using dev::lds_i16x4_t;
+using dev::lds_u32x4_t;
+using dev::make_rsrc;
+using dev::u32x4;
+using dev::wave_max_pair;
+using dev::wave_sum_pair;
+using dev::xcd_remap;
 
 constexpr int kBN = 64;              // keys per tile
 constexpr float kTau = 8.0f;         // lazy-rescale threshold, log2 units
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kLog2e = 1.44269504088896340736f;
-constexpr int kBufferFlags = 0x00020000;  // gfx9 buffer descriptor word 3
 
 struct Params {
   const uint16_t *q, *k, *v;
@@ -122,18 +126,6 @@ struct Geo {
   static constexpr int kPV = 4 * kDB;           // PV MFMAs per tile
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufferFlags);
-}
-
-// Workgroup id -> logical id.  Consecutive hardware ids are dealt round-robin
-// to the 8 XCDs; this gives XCD x one contiguous range of logical ids, so the
-// workgroups sharing one head's K/V run behind one L2.
-__device__ __forceinline__ int xcd_remap(int id, int total) {
-  const int q = total >> 3, r = total & 7;
-  const int x = id & 7, slot = id >> 3;
-  return x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
-}
 
 // This thread's share of one K tile and one V tile (possibly of different
 // key tiles): kLoads 16-byte chunks each.  Chunk n covers tile row
@@ -171,15 +163,6 @@ struct TileStage {
   }
 };
 
-__device__ __forceinline__ float wave_max_pair(float x) {
-  // max of this lane and lane ^ 32
-  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-}
-__device__ __forceinline__ float wave_sum_pair(float x) {
-  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-}
 
 // The key tiles a block of query rows visits: [0, a_hi) then [b_lo, b_hi)
 // (disjoint, a_hi < b_lo).  The first range holds the global keys, the
