@@ -74,6 +74,8 @@ CASES = [
     (1, 4, 4, 1, 128, 4096, [9000], 0),               # large pages
     (3, 4, 2, 8, 128, 16, [8, 7, 40], 5),             # T > L for one sequence
     (2, 32, 4, 4, 128, 64, [70000, 3], 4096),
+    (1, 17, 1, 1, 128, 32, [333], 0),                 # 17 columns: the 32-column kernel
+    (2, 12, 2, 3, 64, 16, [50, 401], 0),              # 18 columns at d = 64
 ]
 
 
