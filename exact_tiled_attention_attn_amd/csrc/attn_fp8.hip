@@ -104,14 +104,14 @@ __global__ __launch_bounds__(256) void attn_fp8_amax_kernel(PackParams pp) {
   for (; i + 3 * stride < n8; i += 4 * stride) {
     bf16x8 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = x[i + u * stride];
+    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(&x[i + u * stride]);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)v[u][e]));
   }
   for (; i < n8; i += stride) {
-    const bf16x8 v = x[i];
+    const bf16x8 v = __builtin_nontemporal_load(&x[i]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)v[e]));
   }
@@ -140,13 +140,13 @@ __global__ __launch_bounds__(256) void attn_fp8_pack_qk_kernel(PackParams pp) {
   const long long n8 = pp.n[t] / 8;
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
        i += (long long)gridDim.x * blockDim.x) {
-    const bf16x8 v = *(const bf16x8 *)(x + 8 * i);
+    const bf16x8 v = __builtin_nontemporal_load((const bf16x8 *)(x + 8 * i));
     int lo = __builtin_amdgcn_cvt_pk_fp8_f32((float)v[0] * inv, (float)v[1] * inv, 0, false);
     lo = __builtin_amdgcn_cvt_pk_fp8_f32((float)v[2] * inv, (float)v[3] * inv, lo, true);
     int hi = __builtin_amdgcn_cvt_pk_fp8_f32((float)v[4] * inv, (float)v[5] * inv, 0, false);
     hi = __builtin_amdgcn_cvt_pk_fp8_f32((float)v[6] * inv, (float)v[7] * inv, hi, true);
     typedef int i32x2 __attribute__((ext_vector_type(2)));
-    *(i32x2 *)(y + 8 * i) = i32x2{lo, hi};
+    __builtin_nontemporal_store(i32x2{lo, hi}, (i32x2 *)(y + 8 * i));
   }
 }
 
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void attn_fp8_pack_vt_kernel(PackParams pp) {
   for (int c = threadIdx.x; c < kBN8 * D / 8; c += blockDim.x) {
     const int r = c / (D / 8), col = 8 * (c % (D / 8));
     u32x4 v = u32x4{};
-    if (j0 + r < pp.N) v = *(const u32x4 *)(src + (size_t)(j0 + r) * D + col);
+    if (j0 + r < pp.N) v = __builtin_nontemporal_load((const u32x4 *)(src + (size_t)(j0 + r) * D + col));
     *(u32x4 *)&tile[r][col] = v;
   }
   __syncthreads();
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256) void attn_fp8_pack_vt_kernel(PackParams pp) {
       int x = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
       w[q] = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], x, true);
     }
-    *(i32x4 *)(dst + (size_t)d * pp.Np + p0) = i32x4{w[0], w[1], w[2], w[3]};
+    __builtin_nontemporal_store(i32x4{w[0], w[1], w[2], w[3]}, (i32x4 *)(dst + (size_t)d * pp.Np + p0));
   }
 }
 
