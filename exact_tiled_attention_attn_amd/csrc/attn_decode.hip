@@ -399,11 +399,11 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int T, int d, int page_size, int 
   if (window > 0 && (long long)window + T - 1 + unit < span) span = (long long)window + T - 1 + unit;
   const long long max_chunk = (long long)kMaxEntries * page_size;  // one table entry per lane
   // about 4096 single-wave workgroups when every sequence is max_seq_len
-  // long: twice the 2048 the GPU holds at once (256 CUs x 4 SIMDs x 2 waves
-  // of 254 VGPRs).  Shorter sequences leave their last splits empty, so a
-  // typical call runs in one to two waves of workgroups.  (Measured on 8
-  // sequences of 12k..102k keys: 3072-4096 in total is 3 % faster than
-  // 8192 and 13 % faster than 2048.)
+  // long: four times the 1024 the GPU holds at once at d = 128 (254 VGPRs
+  // and 144 AGPRs: one wave per SIMD).  Shorter sequences leave their last
+  // splits empty, so a typical call runs in a few rounds of workgroups.
+  // (Measured on 8 sequences of 12k..102k keys: 3072-4096 in total is 3 %
+  // faster than 8192 and 13 % faster than 2048.)
   const long long groups = (long long)B * Hkv;
   long long want = (4096 + groups - 1) / groups;
   long long chunk = (span + want - 1) / want;
