@@ -383,7 +383,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkdv_kernel(BwdParams prm
   };
   // P = exp2(S c - lse log2 e) (zero where masked) and dS = P (dP - Delta),
   // as bf16 B operands
-  auto softmax = [&](auto masked, const lchar *set, int q0, int rb, const f32x16 &sa,
+  auto softmax = [&](bool masked, const lchar *set, int q0, int rb, const f32x16 &sa,
                      const f32x16 &dp, bf16x8 (&pf)[2], bf16x8 (&dsf)[2]) {
     const lds_f32x4_t *lsep = (const lds_f32x4_t *)(set + kLse) + 8 * rb + hh;
     const lds_f32x4_t *delp = (const lds_f32x4_t *)(set + kDel) + 8 * rb + hh;
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkdv_kernel(BwdParams prm
       for (int e = 0; e < 4; ++e)
         p[4 * a + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[4 * a + e], c, -l2[e]));
     }
-    if constexpr (decltype(masked)::value) {
+    if (masked) {
       const int base = q0 + 32 * rb + 4 * hh - m_lo;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkdv_kernel(BwdParams prm
   // much hides under the matrix cores: the S / dP products of block 1 are
   // issued ahead of the softmax of block 0, and the dV / dK products of
   // block 0 ahead of the softmax of block 1.
-  auto tile = [&](auto masked, int q0, const lchar *set) {
+  auto tile = [&](bool masked, int q0, const lchar *set) {
     f32x16 s0, d0, s1, d1;
     bf16x8 p0[2], g0[2], p1[2], g1[2];
     sdp(set, 0, s0, d0);
@@ -449,11 +449,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkdv_kernel(BwdParams prm
     const bool need_mask = (prm.causal && q0 < kw0 + 31) ||
                            (prm.window > 0 && q0 + kBN - 1 >= kw0 + prm.window) ||
                            (q0 + kBN > N) || (kw0 + 31 >= N);
-    if (need_mask) {
-      tile(std::true_type{}, q0, set);
-    } else {
-      tile(std::false_type{}, q0, set);
-    }
+    tile(need_mask, q0, set);
   };
 
   lchar *const set0 = (lchar *)smem;
