@@ -41,6 +41,8 @@ DECODE = ["d1_decode_gqa_128k", "d2_decode_mha_8k", "d3_decode_window_spec4"]
 VARLEN = ["v1_packed_causal_gqa", "l1_longformer_4k"]
 FP8_OTHERS = ["c4_causal_gqa", "c5_long_causal"]
 KERNEL_SRC = os.path.join(ROOT, "exact_tiled_attention_attn_amd", "csrc", "attn_fwd.hip")
+# the forward kernel also compiles the shared device helpers
+KERNEL_HEADERS = [os.path.join(ROOT, "exact_tiled_attention_attn_amd", "csrc", "attn_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -49,15 +51,19 @@ def log(msg):
 
 
 def kernel_sha() -> str:
-    """sha256[:16] of the kernel source with // comments, trailing blanks and
-    empty lines removed: a comment edit keeps stored counter data valid, any
-    code change invalidates it."""
+    """sha256[:16] of the forward kernel's code: its source and the device
+    header it includes, with // comments, trailing blanks and empty lines
+    removed, and the device compile flags.  A comment edit keeps stored
+    counter data valid; any change to the code or the flags invalidates it."""
+    from exact_tiled_attention_attn_amd.build import DEVICE_ONLY, COMMON
     code = []
-    with open(KERNEL_SRC) as f:
-        for line in f:
-            line = line.split("//", 1)[0].rstrip()
-            if line:
-                code.append(line)
+    for path in [KERNEL_SRC] + KERNEL_HEADERS:
+        with open(path) as f:
+            for line in f:
+                line = line.split("//", 1)[0].rstrip()
+                if line:
+                    code.append(line)
+    code.append(" ".join(COMMON + DEVICE_ONLY))
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 

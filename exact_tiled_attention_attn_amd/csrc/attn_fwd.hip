@@ -55,6 +55,7 @@
 #include <cfloat>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "attn_device.h"
 #include "attn_internal.h"
@@ -706,6 +707,430 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D == 64) ? 3 : 2) void attn_fw
   write_out<D>(prm, tk, l32, hh, oacc, st);
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong schedule (8 waves).  The two waves that share a SIMD belong to
+// different groups: A = waves 0-3, B = waves 4-7.  The workgroup advances in
+// half-steps separated by barriers; in every half-step one group runs its
+// matrix phase while the other runs its softmax phase (vector ALU only), and
+// the groups swap at the next barrier, so each SIMD has one wave feeding the
+// matrix pipe while the other computes exponentials.
+//
+// A wave's step m is a matrix phase, S(m + 1) = K(m + 1) Q^T and
+// O += P(m - 1) V(m - 1) (32 MFMAs at d = 128), then a softmax phase that
+// turns S(m) into P(m).  S is computed one tile ahead (two S buffers): a
+// wave's softmax reads S issued a full step earlier, which has left the
+// matrix pipe whatever the other wave queued behind it.
+//
+// Staging: group A loads the K tiles, group B the V tiles, HBM -> LDS
+// directly (no registers), into rings of three K and four V slots; the
+// loads of a matrix phase are spread over its k-steps.
+// ---------------------------------------------------------------------------
+
+// Direct HBM -> LDS load of 16 bytes per lane (buffer_load ... lds): lane l
+// writes LDS bytes lds_addr + 16 l .. + 15, lds_addr taken from M0.  Written
+// as inline asm so that the compiler does not make every barrier and LDS
+// read wait for these loads (it would treat each as an LDS store of unknown
+// extent); the kernel waits for them itself with s_waitcnt vmcnt before the
+// barrier that publishes the tile.  No register receives data.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr,
+                                          uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory");
+}
+
+// Wait until at most N of this wave's vector memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// A K or V tile in LDS, filled by direct loads: its padded rows (K: kCh + 1
+// chunks of 16 bytes, V: kCh + 4) are laid end to end in a region of
+// 64 (kCh + 4) chunks, which the 4 waves of a group fill with kWaveLoads
+// wave-wide loads each (64 consecutive chunks per load).  Chunks that are
+// row padding, or past the 64th row, load from outside the buffer (zero, no
+// memory access).
+template <int D>
+struct DmaTile {
+  using g = Geo<D>;
+  static constexpr int kChunks = kBN * (g::kCh + 4);  // chunks per region
+  static constexpr int kRegionB = kChunks * 16;
+  static constexpr int kWaveLoads = kChunks / 256;    // per wave of a group of 4
+  static_assert(kWaveLoads * 256 == kChunks, "region must split over 4 waves");
+  static constexpr uint32_t kNowhere = 0x40000000u;   // beyond any slice
+
+  uint32_t voff[kWaveLoads];
+
+  // Global byte offsets (relative to the tile's first row) of this lane's
+  // chunks; cpr = chunks per padded row.
+  __device__ __forceinline__ void init(int cpr, int w4, int lane) {
+#pragma unroll
+    for (int i = 0; i < kWaveLoads; ++i) {
+      const int s = 64 * (w4 + 4 * i) + lane;
+      const int row = s / cpr, c = s - row * cpr;
+      voff[i] = (c < g::kCh && row < kBN) ? (uint32_t)(row * g::kRowB + c * 16) : kNowhere;
+    }
+  }
+  // Load i (0 .. kWaveLoads - 1) of this wave's share of the tile starting
+  // at key row j0, into the region at LDS byte address region.
+  __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, uint32_t region, int j0,
+                                            int w4, int i) const {
+    lds_dma16(rs, region + 1024u * (uint32_t)(w4 + 4 * i), voff[i], (uint32_t)j0 * g::kRowB);
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, uint32_t region, int j0,
+                                        int w4) const {
+#pragma unroll
+    for (int i = 0; i < kWaveLoads; ++i) issue_one(rs, region, j0, w4, i);
+  }
+};
+
+// Online softmax of one tile, in place, scheduled for a wave that runs it
+// alone on its SIMD's vector ALU (the other wave is issuing MFMAs): every
+// step is a batch of independent instructions, so each result is used
+// several instructions after it is produced.  The row max first (a max3
+// tree; lazy reference move and rescale as in softmax_core, the rescale of
+// O inside the rare branch), then p = exp2(c * s - m2) overwrites s, packed
+// to bf16 as the B operand of the PV MFMAs, and the fp32 running sum (the
+// sum of the bf16 weights is taken in the next matrix phase).
+template <int KDB>
+__device__ __forceinline__ void softmax_pp(f32x16 (&s)[2], bf16x8 (&pf)[2][2], RowState &st,
+                                           f32x16 (&oacc)[KDB], float c) {
+  auto S = [&](int i) { return s[i >> 4][i & 15]; };
+  float a[10];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) a[i] = fmaxf(fmaxf(S(3 * i), S(3 * i + 1)), S(3 * i + 2));
+  float b3[4];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) b3[j] = fmaxf(fmaxf(a[3 * j], a[3 * j + 1]), a[3 * j + 2]);
+  b3[3] = fmaxf(fmaxf(a[9], S(30)), S(31));
+  const float mx = fmaxf(fmaxf(fmaxf(b3[0], b3[1]), b3[2]), b3[3]);
+  const float mt2 = wave_max_pair(mx) * c;
+  if (__builtin_amdgcn_ballot_w64(mt2 > st.m2 + kTau) != 0) {
+    const float mnew = fmaxf(st.m2, mt2);
+    const float alpha = __builtin_amdgcn_exp2f(st.m2 - mnew);
+    st.lsum *= alpha;
+    st.lrnd *= alpha;
+#pragma unroll
+    for (int i = 0; i < KDB; ++i) oacc[i] *= alpha;
+    st.m2 = mnew;
+  }
+  const float negm = -st.m2;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) s[i >> 4][i & 15] = __builtin_fmaf(S(i), c, negm);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) s[i >> 4][i & 15] = __builtin_amdgcn_exp2f(S(i));
+  __builtin_amdgcn_sched_barrier(0);
+  // register 8 tt + e of block rb is element e of pf[rb][tt]
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[rb][tt][e] = (__bf16)s[rb][8 * tt + e];
+    }
+  }
+  float t[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) t[i] = S(2 * i) + S(2 * i + 1);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] += t[i + 8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t[i] += t[i + 4];
+  t[0] += t[2];
+  t[1] += t[3];
+  st.lsum += t[0] + t[1];
+}
+
+// The matrix phase: S^T = K Q^T (DO_S) and O^T += V^T P^T (DO_PV),
+// interleaved two MFMAs of each per k-step; hook(j) runs at the start of
+// k-step j (the tile loads, spread over the phase).  On entry ka[0], ka[1]
+// hold the K fragments of k-steps 0 and 1 and va[0..3] the first four V^T
+// fragments.
+template <int D, bool DO_S, bool DO_PV, class Hook>
+__device__ __forceinline__ void mfma_phase(const lchar *kb, const lchar *vb,
+                                           const bf16x8 (&qf)[Geo<D>::kKSteps], f32x16 (&s)[2],
+                                           const bf16x8 (&pf)[2][2],
+                                           f32x16 (&oacc)[Geo<D>::kDB], bf16x8 (&ka)[3][2],
+                                           bf16x8 (&va)[4], float &lrnd, Hook &&hook) {
+  using g = Geo<D>;
+  static_assert(g::kPV == 2 * g::kKSteps, "two PV MFMAs per S k-step");
+  // The sum of the bf16 weights as the PV MFMAs use them (O is normalized by
+  // it): one v_dot2 against (1, 1) per packed pair of weights, issued between
+  // the MFMAs (in the softmax phase these wait for the other wave's MFMAs).
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float rp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto vf = [&](int i) { return vfrag<D>(vb, i >> 2, (i >> 1) & 1, i & 1); };
+  if constexpr (DO_S) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+  }
+#pragma unroll
+  for (int j = 0; j < g::kKSteps; ++j) {
+    hook(j);
+    if constexpr (DO_S) {
+      if (j + 2 < g::kKSteps) {
+        ka[(j + 2) % 3][0] = kfrag<D>(kb, j + 2, 0);
+        ka[(j + 2) % 3][1] = kfrag<D>(kb, j + 2, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j % 3][0], qf[j], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j % 3][1], qf[j], s[1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (DO_PV) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = 2 * j + u;
+        const int db = i >> 2, rb = (i >> 1) & 1, tt = i & 1;
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 4], pf[rb][tt], oacc[db], 0, 0, 0);
+        if (i + 4 < g::kPV) va[i % 4] = vf(i + 4);
+#pragma unroll
+        for (int t = 0; t < 16 / g::kPV; ++t) {  // pair n: word n % 4 of pf[n / 8][(n / 4) % 2]
+          const int n = i * (16 / g::kPV) + t;
+          const bf16x8 &w = pf[n >> 3][(n >> 2) & 1];
+          const bf16x2 pair = {w[2 * (n & 3)], w[2 * (n & 3) + 1]};
+          rp[n & 3] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, rp[n & 3], false);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  if constexpr (DO_PV) lrnd += (rp[0] + rp[1]) + (rp[2] + rp[3]);
+}
+
+template <int D, int P, bool GEN>
+__global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(Params prm) {
+  using g = Geo<D>;
+  constexpr int kRows = 32 * 8 / P;  // query rows per workgroup
+  using dt = DmaTile<D>;
+  constexpr int kKSlots = 3;  // K ring
+  constexpr int kVSlots = 4;  // V ring
+  static_assert(g::kVTileB == dt::kRegionB, "a V tile fills its region");
+
+  __shared__ __attribute__((aligned(1024))) char smem[(kKSlots + kVSlots) * dt::kRegionB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: group A (stages K), 1: group B (stages V)
+  const int gt = tid & 255;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  const Task tk = make_task<P, kRows, GEN>(prm, wave);
+  if (tk.empty) return;  // the whole workgroup
+  const int N = tk.N;
+  const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(prm.k + tk.kv_slice * D, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(prm.v + tk.kv_slice * D, (uint32_t)N * D * 2);
+
+  bf16x8 qf[g::kKSteps];
+  load_q<D>(prm, tk, l32, hh, qf);
+  const int k_lane = k_lane_off<D>(lane);
+  const int v_lane = v_lane_off<D>(lane);
+
+  f32x16 oacc[g::kDB];
+#pragma unroll
+  for (int i = 0; i < g::kDB; ++i) oacc[i] = f32x16{};
+  RowState st;
+  const float c = prm.c;
+#pragma unroll
+  for (int kk = 0; kk < g::kKSteps; ++kk) asm volatile("" : "+v"(qf[kk]) : : "memory");
+
+  const int count = tk.wg.count();
+  auto row_of = [&](int k) { return k < count ? tk.wg.tile(k) * kBN : N; };
+  auto ktile = [&](int j) { return (lchar *)smem + (j % kKSlots) * dt::kRegionB; };
+  auto vtile = [&](int j) {
+    return (lchar *)smem + (kKSlots + (j & (kVSlots - 1))) * dt::kRegionB;
+  };
+  auto sees = [&](int m) { return m < count && tk.w.has(tk.wg.tile(m)); };
+
+  // S of two tiles in flight: S(m) in sb[m % 2] is turned into weights while
+  // the MFMAs of S(m + 1) run.
+  f32x16 sb[2][2];
+  bf16x8 pf[2][2];
+  bf16x8 ka[3][2];
+  bf16x8 va[4];
+
+  // Group A stages K, group B stages V.
+  auto group_program = [&](auto grp_c) {
+    constexpr int G = decltype(grp_c)::value;
+    const int w4 = wave & 3;
+    // Step m >= 1 reads K(m + 1) (half-steps 2m, group A, and 2m + 1, group
+    // B), step 0 reads K(0) and K(1); V(j) is read in half-steps 2j + 2 and
+    // 2j + 3.  A slot's next tile is loaded (straight into LDS) once both
+    // groups have read the previous one: group A loads K(m + 3) in its
+    // matrix phase of step m >= 1 (K(3) too in step 1) and waits for K(m + 2)
+    // at the end of its softmax phase; group B loads V(m + 2) in its matrix
+    // phase of step m and waits for V(m) at its end.  The loads are spread
+    // over the phase's k-steps.  Loads past the last tile read outside the
+    // buffer (zero, no memory access), so the number of loads in flight does
+    // not depend on the tile count.
+    const __amdgpu_buffer_rsrc_t rs = G == 0 ? rs_k : rs_v;
+    dt dma;
+    dma.init(G == 0 ? g::kCh + 1 : g::kCh + 4, w4, lane);
+    auto region = [&](int j) { return (uint32_t)(uintptr_t)(G == 0 ? ktile(j) : vtile(j)); };
+    if constexpr (G == 0) {
+      dma.issue(rs, region(0), row_of(0), w4);
+      dma.issue(rs, region(1), row_of(1), w4);
+      dma.issue(rs, region(2), row_of(2), w4);
+      wait_loads<dt::kWaveLoads>();
+    } else {
+      dma.issue(rs, region(0), row_of(0), w4);
+      dma.issue(rs, region(1), row_of(1), w4);
+    }
+    __syncthreads();
+    if (G == 1) __syncthreads();  // group B runs one half-step behind
+
+    // the loads of the matrix phase of step m, load i at k-step i
+    auto loads = [&](int m) {
+      return [&, m](int i) {
+        if (i < dt::kWaveLoads) {
+          if constexpr (G == 0) {
+            if (m == 1) dma.issue_one(rs, region(3), row_of(3), w4, i);
+            if (m >= 1) dma.issue_one(rs, region(m + 3), row_of(m + 3), w4, i);
+          } else {
+            dma.issue_one(rs, region(m + 2), row_of(m + 2), w4, i);
+          }
+        }
+      };
+    };
+    auto no_loads = [](int) {};
+    auto prefetch_k = [&](int j) {  // K fragments of k-steps 0, 1 of tile j
+      const lchar *kb = ktile(j) + k_lane;
+      ka[0][0] = kfrag<D>(kb, 0, 0);
+      ka[0][1] = kfrag<D>(kb, 0, 1);
+      ka[1][0] = kfrag<D>(kb, 1, 0);
+      ka[1][1] = kfrag<D>(kb, 1, 1);
+    };
+    auto prefetch_v = [&](int j) {  // the first four V^T fragments of tile j
+      const lchar *vb = vtile(j) + v_lane;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) va[i] = vfrag<D>(vb, i >> 2, (i >> 1) & 1, i & 1);
+    };
+    // Softmax phase of step m: weights P(m) from S(m) (zero if no row of
+    // the wave sees tile m).
+    auto vector = [&](int m, f32x16 (&s)[2]) {
+      if (sees(m)) {
+        mask_tile<GEN>(s, prm, tk.wg.tile(m) * kBN, tk.qw0, l32, hh, N);
+        softmax_pp<g::kDB>(s, pf, st, oacc, c);
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) pf[rb][tt] = bf16x8{};
+        }
+      }
+    };
+    // Matrix phase of step m: S(m + 1) and O += P(m - 1) V(m - 1).  Every
+    // wave runs the same MFMAs whatever its rows see (S of a tile past the
+    // last is computed from whatever the slot holds and never used): one
+    // code path keeps O in the same registers throughout.
+    auto matrix = [&](int m, f32x16 (&s_next)[2]) {
+      __builtin_amdgcn_s_setprio(2);
+      prefetch_k(m + 1);
+      prefetch_v(m - 1);
+      mfma_phase<D, true, true>(ktile(m + 1) + k_lane, vtile(m - 1) + v_lane, qf, s_next, pf,
+                                oacc, ka, va, st.lrnd, loads(m));
+      __builtin_amdgcn_s_setprio(0);
+      if constexpr (G == 1) wait_loads<2 * dt::kWaveLoads>();
+      __syncthreads();
+    };
+
+    // step 0: S(0) and S(1)
+    __builtin_amdgcn_s_setprio(2);
+    prefetch_k(0);
+    mfma_phase<D, true, false>(ktile(0) + k_lane, nullptr, qf, sb[0], pf, oacc, ka, va,
+                               st.lrnd, loads(0));
+    prefetch_k(1);
+    mfma_phase<D, true, false>(ktile(1) + k_lane, nullptr, qf, sb[1], pf, oacc, ka, va,
+                               st.lrnd, no_loads);
+    __builtin_amdgcn_s_setprio(0);
+    if constexpr (G == 1) wait_loads<2 * dt::kWaveLoads>();
+    __syncthreads();
+    vector(0, sb[0]);
+    if constexpr (G == 0) wait_loads<0>();
+    __syncthreads();
+    int m = 1;
+    for (;;) {
+      if (m == count) break;
+      matrix(m, sb[0]);  // S(m + 1), m odd
+      vector(m, sb[1]);
+      if constexpr (G == 0) {
+        // K(m + 2): after step 1, whose loads of K(3) and K(4) interleave,
+        // wait for all of them
+        if (m == 1) {
+          wait_loads<0>();
+        } else {
+          wait_loads<dt::kWaveLoads>();
+        }
+      }
+      __syncthreads();
+      ++m;
+      if (m == count) break;
+      matrix(m, sb[1]);  // S(m + 1), m even
+      vector(m, sb[0]);
+      if constexpr (G == 0) wait_loads<dt::kWaveLoads>();
+      __syncthreads();
+      ++m;
+    }
+    // last step: O += P(count - 1) V(count - 1)
+    __builtin_amdgcn_s_setprio(2);
+    prefetch_v(count - 1);
+    mfma_phase<D, false, true>(nullptr, vtile(count - 1) + v_lane, qf, sb[0], pf, oacc, ka, va,
+                               st.lrnd, no_loads);
+    __builtin_amdgcn_s_setprio(0);
+    __syncthreads();
+    if (G == 0) __syncthreads();
+  };
+  if (grp == 0) {
+    group_program(std::integral_constant<int, 0>{});
+  } else {
+    group_program(std::integral_constant<int, 1>{});
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load left in flight
+
+  write_out<D>(prm, tk, l32, hh, oacc, st);
+}
+
+template <int D, int P>
+hipError_t launch_pp_t(const FwdProblem &p, hipStream_t stream) {
+  constexpr int kRows = 32 * 8 / P;
+  Params prm{};
+  prm.q = static_cast<const uint16_t *>(p.q);
+  prm.k = static_cast<const uint16_t *>(p.k);
+  prm.v = static_cast<const uint16_t *>(p.v);
+  prm.o = static_cast<uint16_t *>(p.o);
+  prm.lse = p.lse;
+  prm.B = p.B; prm.Hq = p.Hq; prm.Hkv = p.Hkv; prm.N = p.N;
+  prm.G = p.Hq / p.Hkv;
+  prm.groups = p.Hq / P;
+  prm.nq = (p.N + kRows - 1) / kRows;
+  const long long total = (long long)p.B * prm.groups * prm.nq;
+  if (total > 0x7fffffffLL) return hipErrorInvalidValue;
+  prm.total = (int)total;
+  prm.nkt = (p.N + kBN - 1) / kBN;
+  const float c = std::fabs(p.scale) * kLog2e;
+  prm.c = c < FLT_MIN ? FLT_MIN : c;
+  prm.neg = p.scale < 0.0f ? 1 : 0;
+  prm.causal = p.causal;
+  prm.window = p.window;
+  void *args[] = {&prm};
+  return hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_pp_kernel<D, P, false>),
+                         dim3(prm.total), dim3(512), args, 0, stream);
+}
+
+template <int D>
+hipError_t launch_pp(const FwdProblem &p, hipStream_t stream) {
+  const int G = p.Hq / p.Hkv;
+  if (G % 8 == 0) return launch_pp_t<D, 8>(p, stream);
+  if (G % 4 == 0) return launch_pp_t<D, 4>(p, stream);
+  if (G % 2 == 0) return launch_pp_t<D, 2>(p, stream);
+  return launch_pp_t<D, 1>(p, stream);
+}
+
 template <int D, int NW, int P>
 hipError_t launch_t(const FwdProblem &p, hipStream_t stream) {
   constexpr int kRows = 32 * NW / P;
@@ -773,9 +1198,47 @@ hipError_t launch_gen_t(const VarlenProblem &p, hipStream_t stream) {
                          dim3(prm.total), dim3(NW * 64), args, 0, stream);
 }
 
+template <int D, int P>
+hipError_t launch_gen_pp_t(const VarlenProblem &p, hipStream_t stream) {
+  constexpr int kRows = 32 * 8 / P;
+  Params prm{};
+  prm.q = static_cast<const uint16_t *>(p.q);
+  prm.k = static_cast<const uint16_t *>(p.k);
+  prm.v = static_cast<const uint16_t *>(p.v);
+  prm.o = static_cast<uint16_t *>(p.o);
+  prm.lse = p.lse;
+  prm.B = p.B; prm.Hq = p.Hq; prm.Hkv = p.Hkv; prm.N = p.max_seqlen;
+  prm.G = p.Hq / p.Hkv;
+  prm.groups = p.Hq / P;
+  prm.nq = (p.max_seqlen + kRows - 1) / kRows;
+  const long long total = (long long)p.B * prm.groups * prm.nq;
+  if (total > 0x7fffffffLL) return hipErrorInvalidValue;
+  prm.total = (int)total;
+  prm.nkt = (p.max_seqlen + kBN - 1) / kBN;
+  const float c = std::fabs(p.scale) * kLog2e;
+  prm.c = c < FLT_MIN ? FLT_MIN : c;
+  prm.neg = p.scale < 0.0f ? 1 : 0;
+  prm.causal = p.causal;
+  prm.window = p.window;
+  prm.cu = p.cu_seqlens;
+  prm.total_rows = p.total_rows;
+  prm.radius = p.radius;
+  prm.nglob = p.n_global;
+  prm.compact = (long long)p.B * p.max_seqlen != p.total_rows;
+  void *args[] = {&prm};
+  return hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_pp_kernel<D, P, true>),
+                         dim3(prm.total), dim3(512), args, 0, stream);
+}
+
 template <int D>
 hipError_t launch_gen_d(const VarlenProblem &p, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
+  if constexpr (D == 128) {  // the ping-pong kernel, as the dense default
+    if (G % 8 == 0) return launch_gen_pp_t<D, 8>(p, stream);
+    if (G % 4 == 0) return launch_gen_pp_t<D, 4>(p, stream);
+    if (G % 2 == 0) return launch_gen_pp_t<D, 2>(p, stream);
+    return launch_gen_pp_t<D, 1>(p, stream);
+  }
   if constexpr (kGenWaves<D> >= 8) {
     if (G % 8 == 0) return launch_gen_t<D, 8>(p, stream);
   }
@@ -798,6 +1261,7 @@ hipError_t launch_nw(const FwdProblem &p, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_d(const FwdProblem &p, int v, hipStream_t stream) {
+  if (v == kPingPong) return launch_pp<D>(p, stream);
   return v == kWaves4 ? launch_nw<D, 4>(p, stream) : launch_nw<D, 8>(p, stream);
 }
 
@@ -808,6 +1272,7 @@ const char *variant_name(int variant) {
     case kAuto: return "auto";
     case kWaves4: return "w4_bn64_mfma32x32x16";
     case kWaves8: return "w8_bn64_mfma32x32x16";
+    case kPingPong: return "w8_pingpong_bn64_mfma32x32x16";
   }
   return "invalid";
 }
@@ -815,7 +1280,7 @@ const char *variant_name(int variant) {
 hipError_t launch_fwd(const FwdProblem &p, int variant, hipStream_t stream) {
   // default: 8 waves at d = 128 (one workgroup per CU); 4 waves at d = 64,
   // where 138 VGPRs let three 4-wave workgroups share a CU
-  const int v = variant != kAuto ? variant : p.d == 64 ? kWaves4 : kWaves8;
+  const int v = variant != kAuto ? variant : p.d == 64 ? kWaves4 : kPingPong;
   return p.d == 128 ? launch_d<128>(p, v, stream) : launch_d<64>(p, v, stream);
 }
 

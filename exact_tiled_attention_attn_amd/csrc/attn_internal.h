@@ -24,7 +24,8 @@ enum Variant : int {
   kAuto = 0,
   kWaves4 = 1,  // 4 waves (256 threads) per workgroup, 32 query rows per wave
   kWaves8 = 2,  // 8 waves (512 threads) per workgroup, 32 query rows per wave
-  kNumVariants = 3
+  kPingPong = 3,  // 8 waves in two groups that alternate matrix and softmax phases
+  kNumVariants = 4
 };
 
 const char *variant_name(int variant);

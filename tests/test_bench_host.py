@@ -22,13 +22,32 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 def test_kernel_sha_ignores_comments_and_blank_lines(tmp_path, monkeypatch):
     src = tmp_path / "k.hip"
+    hdr = tmp_path / "h.h"
     src.write_text("int a = 1;  // one\n\n// a comment line\nint b = 2;\n")
+    hdr.write_text("int c = 3;\n")
     monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
+    monkeypatch.setattr(bench, "KERNEL_HEADERS", [str(hdr)])
     h1 = bench.kernel_sha()
     src.write_text("int a = 1;   \n// another comment\nint b = 2;  // two\n\n")
     assert bench.kernel_sha() == h1
     src.write_text("int a = 1;\nint b = 3;\n")
     assert bench.kernel_sha() != h1
+
+
+def test_kernel_sha_covers_the_device_header_and_flags(tmp_path, monkeypatch):
+    from exact_tiled_attention_attn_amd import build
+    src = tmp_path / "k.hip"
+    hdr = tmp_path / "h.h"
+    src.write_text("int a = 1;\n")
+    hdr.write_text("int c = 3;\n")
+    monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
+    monkeypatch.setattr(bench, "KERNEL_HEADERS", [str(hdr)])
+    h1 = bench.kernel_sha()
+    hdr.write_text("int c = 4;\n")
+    h2 = bench.kernel_sha()
+    assert h2 != h1
+    monkeypatch.setattr(build, "DEVICE_ONLY", build.DEVICE_ONLY + ["-DX"])
+    assert bench.kernel_sha() != h2
 
 
 def test_traffic_only_for_the_source_it_was_taken_on(tmp_path, monkeypatch):

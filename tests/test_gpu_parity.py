@@ -86,7 +86,7 @@ SHAPES = [
 ]
 
 
-VARIANTS = [1, 2]  # every explicit kernel variant
+VARIANTS = [1, 2, 3]  # every explicit kernel variant
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -102,11 +102,15 @@ def test_parity_small_shapes(shape, variant):
 
 
 def test_variants_agree():
+    """Every variant meets the oracle bar on its own (above); here they agree
+    with each other to two bf16 ulps on O (they differ in summation order and
+    in which weight sum normalizes O) and to 1e-4 on lse."""
     q, k, v = make_qkv(1, 8, 2, 700, 128, seed=5)
     a = run(q, k, v, True, 300, variant=1)
     for var in VARIANTS[1:]:
         b = run(q, k, v, True, 300, variant=var)
-        assert torch.equal(a[0], b[0]) or (a[0].float() - b[0].float()).abs().max() < 1e-2
+        ao, bo = a[0].float(), b[0].float()
+        assert bool(((ao - bo).abs() <= 2.0 ** -6 * ao.abs() + 1e-3).all()), var
         assert (a[1] - b[1]).abs().max() < 1e-4
 
 
