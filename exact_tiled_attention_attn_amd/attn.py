@@ -99,6 +99,30 @@ def _stream(stream, *tensors):
     return stream.cuda_stream or None
 
 
+def _check_out(t, shape, dtype, device, name):
+    """A caller-supplied output buffer must have exactly the shape, dtype and
+    device the call writes, and be contiguous (the kernels write it densely)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise AttnError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device:
+        raise AttnError(f"{name} must be {tuple(shape)} {dtype} on {device}, "
+                        f"got {tuple(t.shape)} {t.dtype} on {t.device}")
+    if not t.is_contiguous():
+        raise AttnError(f"{name} must be contiguous")
+
+
+def _check_workspace(ws, nbytes, device, name="workspace"):
+    """A caller-supplied workspace must hold at least the bytes the C side
+    asks for (the C entry point cannot check the size it is given)."""
+    import torch
+    if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
+        raise AttnError(f"{name} must be a contiguous tensor on {device}")
+    have = ws.numel() * ws.element_size()
+    if have < nbytes:
+        raise AttnError(f"{name} holds {have} bytes, the call needs {nbytes}")
+
+
 def attn_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, window, stream=None):
     """Call the C entry point; returns its status code (0 = ATTN_OK).
 
@@ -228,6 +252,8 @@ def fwd(q, k, v, causal=False, window=0, scale=None, variant=0, out=None, stream
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     else:
         o, lse = out
+        _check_out(o, q.shape, torch.bfloat16, q.device, "o")
+        _check_out(lse, (B, Hq, N), torch.float32, q.device, "lse")
     st = attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, int(bool(causal)), int(window),
                      variant, stream)
     if st != ATTN_OK:
@@ -266,9 +292,14 @@ def bwd(q, k, v, o, lse, dout, causal=False, window=0, scale=None, out=None, wor
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
         dq, dk, dv = out
+        _check_out(dq, q.shape, torch.bfloat16, q.device, "dq")
+        _check_out(dk, k.shape, torch.bfloat16, q.device, "dk")
+        _check_out(dv, v.shape, torch.bfloat16, q.device, "dv")
+    nbytes = attn_bwd_workspace_size(B, Hq, N)
     if workspace is None:
-        nbytes = attn_bwd_workspace_size(B, Hq, N)
         workspace = torch.empty((max(nbytes, 4) // 4,), dtype=torch.float32, device=q.device)
+    else:
+        _check_workspace(workspace, nbytes, q.device)
     st = attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, scale,
                   int(bool(causal)), int(window), stream)
     if st != ATTN_OK:
@@ -311,10 +342,14 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, window=0, sc
         lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
     else:
         o, lse = out
+        _check_out(o, q.shape, torch.bfloat16, q.device, "o")
+        _check_out(lse, (B, Hq, T), torch.float32, q.device, "lse")
+    nbytes = attn_decode_workspace_size(B, Hq, Hkv, T, d, page_size, max_seq_len,
+                                        max(int(window), 0))
     if workspace is None:
-        nbytes = attn_decode_workspace_size(B, Hq, Hkv, T, d, page_size, max_seq_len,
-                                            max(int(window), 0))
         workspace = torch.empty((max(nbytes, 16) // 4,), dtype=torch.float32, device=q.device)
+    else:
+        _check_workspace(workspace, nbytes, q.device)
     st = attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, workspace, B, Hq,
                            Hkv, T, d, page_size, num_pages, block_table.shape[1], max_seq_len,
                            scale, int(window), stream)
@@ -354,6 +389,8 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, window=0, radius=0
         lse = torch.empty((Hq, total), dtype=torch.float32, device=q.device)
     else:
         o, lse = out
+        _check_out(o, q.shape, torch.bfloat16, q.device, "o")
+        _check_out(lse, (Hq, total), torch.float32, q.device, "lse")
     st = attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, max_seqlen, total, Hq, Hkv, d, scale,
                          int(bool(causal)), int(window), int(radius), int(n_global), stream)
     if st != ATTN_OK:
@@ -394,6 +431,8 @@ def fwd_fp8(q8, k8, vt8, scales, causal=False, window=0, scale=None, out=None, s
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device)
     else:
         o, lse = out
+        _check_out(o, (B, Hq, N, d), torch.bfloat16, q8.device, "o")
+        _check_out(lse, (B, Hq, N), torch.float32, q8.device, "lse")
     st = attn_fwd_fp8(q8, k8, vt8, scales, o, lse, B, Hq, Hkv, N, d, scale, int(bool(causal)),
                       int(window), stream)
     if st != ATTN_OK:

@@ -125,6 +125,29 @@ def test_fwd_wrapper_rejects_host_tensors(lib):
         attn.fwd(q, q, q)
 
 
+def test_caller_buffers_are_checked_before_the_call():
+    """out= buffers and workspaces the caller passes are checked in the
+    binding (the C entry points cannot see their extent); the same helpers
+    run in fwd, fwd_varlen, fwd_fp8, bwd and decode before the call."""
+    import torch
+    dev = torch.device("cpu")
+    good = torch.empty((2, 3, 4), dtype=torch.bfloat16)
+    attn._check_out(good, (2, 3, 4), torch.bfloat16, dev, "o")
+    for bad in (torch.empty((2, 3, 5), dtype=torch.bfloat16),
+                torch.empty((2, 3, 4), dtype=torch.float32),
+                torch.empty((2, 4, 3), dtype=torch.bfloat16).transpose(1, 2)):
+        with pytest.raises(attn.AttnError):
+            attn._check_out(bad, (2, 3, 4), torch.bfloat16, dev, "o")
+    with pytest.raises(attn.AttnError):
+        attn._check_out(good, (2, 3, 4), torch.bfloat16, torch.device("meta"), "o")
+    ws = torch.empty((100,), dtype=torch.float32)
+    attn._check_workspace(ws, 400, dev)
+    with pytest.raises(attn.AttnError):
+        attn._check_workspace(ws, 401, dev)
+    with pytest.raises(attn.AttnError):
+        attn._check_workspace(torch.empty((10, 20), dtype=torch.float32).t(), 4, dev)
+
+
 BWD_GOOD = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, workspace=P, B=1, Hq=4,
                 Hkv=2, N=64, d=128, scale=0.1, causal=1, window=0)
 
