@@ -19,11 +19,14 @@ ATTN_OK = 0
 ATTN_ERR_INVALID_ARG = 1
 ATTN_ERR_UNSUPPORTED = 2
 ATTN_ERR_LAUNCH = 3
+ATTN_ERR_NO_SCRATCH = 4
 ATTN_MAX_N = 1 << 22
+ATTN_DECODE_NOALLOC_MAX_BYTES = 32 << 20
 
 EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_fwd_fp8", "attn_fp8_quantize",
             "attn_fp8_vt_bytes", "attn_bwd", "attn_bwd_workspace_size",
-            "attn_decode_paged", "attn_decode_workspace_size", "attn_num_variants",
+            "attn_decode_paged", "attn_decode_workspace_size", "attn_decode_paged_noalloc",
+            "attn_num_variants",
             "attn_variant_name", "attn_status_string", "attn_abi_version")
 
 
@@ -68,6 +71,8 @@ def load_library():
     lib.attn_decode_paged.restype = i
     lib.attn_decode_workspace_size.argtypes = [i] * 8
     lib.attn_decode_workspace_size.restype = ctypes.c_size_t
+    lib.attn_decode_paged_noalloc.argtypes = [vp] * 7 + [i] * 9 + [f, i, vp]
+    lib.attn_decode_paged_noalloc.restype = i
     lib.attn_num_variants.argtypes = []
     lib.attn_num_variants.restype = i
     lib.attn_variant_name.argtypes = [i]
@@ -200,6 +205,18 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, worksp
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(o),
         _ptr(lse), _ptr(workspace), int(B), int(Hq), int(Hkv), int(T), int(d), int(page_size),
         int(num_pages), int(max_pages_per_seq), int(max_seq_len), float(scale), int(window),
+        _stream(stream, q, k_cache, v_cache, o, lse))
+
+
+def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, Hq, Hkv,
+                              T, d, page_size, num_pages, max_pages_per_seq, max_seq_len, scale,
+                              window, stream=None):
+    """Call the C allocation-free paged-decode entry point; returns its status."""
+    lib = load_library()
+    return lib.attn_decode_paged_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(o),
+        _ptr(lse), int(B), int(Hq), int(Hkv), int(T), int(d), int(page_size), int(num_pages),
+        int(max_pages_per_seq), int(max_seq_len), float(scale), int(window),
         _stream(stream, q, k_cache, v_cache, o, lse))
 
 

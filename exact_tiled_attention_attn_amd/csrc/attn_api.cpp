@@ -72,7 +72,7 @@ attn_status_t validate_varlen(const attn::VarlenProblem &p) {
 
 bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 
-attn_status_t validate_decode(const attn::DecodeProblem &p) {
+attn_status_t validate_decode(const attn::DecodeProblem &p, bool need_workspace = true) {
   if (p.B < 0 || p.T < 1 || p.num_pages < 0 || p.max_pages < 0 || p.max_seq_len < 0)
     return ATTN_ERR_INVALID_ARG;
   if (p.Hq < 1 || p.Hkv < 1 || p.Hq % p.Hkv != 0) return ATTN_ERR_INVALID_ARG;
@@ -83,11 +83,11 @@ attn_status_t validate_decode(const attn::DecodeProblem &p) {
   if (p.max_seq_len > ATTN_MAX_N) return ATTN_ERR_UNSUPPORTED;
   if (p.B == 0 || p.max_seq_len == 0) return ATTN_OK;  // nothing to read or write
   if (!p.q || !p.k_cache || !p.v_cache || !p.block_table || !p.seq_lens || !p.o || !p.lse ||
-      !p.workspace)
+      (need_workspace && !p.workspace))
     return ATTN_ERR_INVALID_ARG;
   if (p.num_pages < 1 || p.max_pages < 1) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(p.q) || !aligned16(p.k_cache) || !aligned16(p.v_cache) || !aligned16(p.o) ||
-      !aligned16(p.lse) || !aligned16(p.workspace) ||
+      !aligned16(p.lse) || (need_workspace && !aligned16(p.workspace)) ||
       (reinterpret_cast<uintptr_t>(p.block_table) & 3u) != 0 ||
       (reinterpret_cast<uintptr_t>(p.seq_lens) & 3u) != 0)
     return ATTN_ERR_UNSUPPORTED;
@@ -223,6 +223,29 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+attn_status_t attn_decode_paged_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                        const int *block_table, const int *seq_lens, void *o,
+                                        float *lse, int B, int Hq, int Hkv, int T, int d,
+                                        int page_size, int num_pages, int max_pages_per_seq,
+                                        int max_seq_len, float scale, int window, void *stream) {
+  attn::DecodeProblem p{q,  k_cache, v_cache, block_table, seq_lens,          o,
+                        lse, nullptr, B,      Hq,          Hkv,               T,
+                        d,  page_size, num_pages, max_pages_per_seq, max_seq_len, scale,
+                        window};
+  const attn_status_t st = validate_decode(p, false);
+  if (st != ATTN_OK) return st;
+  if (B == 0 || max_seq_len == 0) return ATTN_OK;
+  if (p.window < 0) p.window = 0;
+  const attn::DecodePlan plan =
+      attn::plan_decode(B, Hq, Hkv, T, d, page_size, max_seq_len, p.window);
+  if ((plan.part_o_floats + plan.part_lse_floats) * sizeof(float) > ATTN_DECODE_NOALLOC_MAX_BYTES)
+    return ATTN_ERR_NO_SCRATCH;
+  if (attn::decode_noalloc_scratch(&p.workspace) != hipSuccess) return ATTN_ERR_NO_SCRATCH;
+  const hipError_t e = attn::launch_decode(p, plan, static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidValue) return ATTN_ERR_UNSUPPORTED;
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 int attn_num_variants(void) { return attn::kNumVariants; }
 
 const char *attn_variant_name(int variant) { return attn::variant_name(variant); }
@@ -233,6 +256,7 @@ const char *attn_status_string(attn_status_t status) {
     case ATTN_ERR_INVALID_ARG: return "invalid argument";
     case ATTN_ERR_UNSUPPORTED: return "unsupported problem";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    case ATTN_ERR_NO_SCRATCH: return "problem exceeds the allocation-free scratch";
   }
   return "unknown status";
 }

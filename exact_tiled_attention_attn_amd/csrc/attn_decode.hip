@@ -33,6 +33,9 @@
 #include <cmath>
 #include <cstdint>
 
+#include <mutex>
+
+#include "attn.h"
 #include "attn_device.h"
 #include "attn_internal.h"
 
@@ -420,6 +423,34 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int T, int d, int page_size, int 
 
 hipError_t launch_decode(const DecodeProblem &p, const DecodePlan &plan, hipStream_t stream) {
   return p.d == 128 ? launch_decode_d<128>(p, plan, stream) : launch_decode_d<64>(p, plan, stream);
+}
+
+// Scratch of the allocation-free decode entry point: the split partials
+// (partial O then partial lse, as in the workspace of attn_decode_paged).
+// Every split writes its slot before the merge reads it, so nothing needs
+// clearing between calls.  One copy per GPU, at its own address.
+static __device__ __align__(256) float scratch[ATTN_DECODE_NOALLOC_MAX_BYTES / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_noalloc_scratch(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace attn

@@ -112,4 +112,8 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int T, int d, int page_size, int 
 // Enqueue the split kernel and the merge kernel for `p` on `stream`.
 hipError_t launch_decode(const DecodeProblem &p, const DecodePlan &plan, hipStream_t stream);
 
+// Device address of the allocation-free decode's scratch array on the
+// current device (looked up once per device).
+hipError_t decode_noalloc_scratch(void **ptr);
+
 }  // namespace attn

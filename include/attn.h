@@ -64,7 +64,11 @@ typedef enum attn_status {
    * N > ATTN_MAX_N, or a variant that cannot run this problem */
   ATTN_ERR_UNSUPPORTED = 2,
   /* the HIP launch itself failed (hipLaunchKernel returned an error) */
-  ATTN_ERR_LAUNCH = 3
+  ATTN_ERR_LAUNCH = 3,
+  /* attn_decode_paged_noalloc: the problem needs more scratch than the
+   * library's fixed array (ATTN_DECODE_NOALLOC_MAX_BYTES), or the array's
+   * device address could not be obtained */
+  ATTN_ERR_NO_SCRATCH = 4
 } attn_status_t;
 
 /* Longest sequence accepted.  The kernels address one (batch, head) slice of
@@ -256,6 +260,27 @@ attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int T, int d, int page_size,
                                   int max_seq_len, int window);
 
+/* Paged decode that allocates nothing, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  attn_decode_paged's operation and
+ * arguments without the workspace: the split partials go to a scratch array
+ * of ATTN_DECODE_NOALLOC_MAX_BYTES bytes that the library keeps in the
+ * device memory of each GPU it runs on (its address is looked up on the
+ * first call on a device, which must then be the current device; the array
+ * lives until the process ends).  A problem whose
+ * attn_decode_workspace_size(...) exceeds that returns ATTN_ERR_NO_SCRATCH
+ * and launches nothing; otherwise errors as for attn_decode_paged.  The
+ * call uses no allocating routine.  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be serialized by the caller.  `stream` must belong
+ * to the current device. */
+#define ATTN_DECODE_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+attn_status_t attn_decode_paged_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                        const int *block_table, const int *seq_lens, void *o,
+                                        float *lse, int B, int Hq, int Hkv, int T, int d,
+                                        int page_size, int num_pages, int max_pages_per_seq,
+                                        int max_seq_len, float scale, int window, void *stream);
+
 /* Number of variant ids accepted by attn_fwd_ex (ids 0 .. n-1). */
 int attn_num_variants(void);
 
@@ -266,7 +291,7 @@ const char *attn_variant_name(int variant);
 const char *attn_status_string(attn_status_t status);
 
 /* ABI version of this header (incremented on any signature change). */
-#define ATTN_ABI_VERSION 5
+#define ATTN_ABI_VERSION 6
 int attn_abi_version(void);
 
 #ifdef __cplusplus

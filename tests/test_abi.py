@@ -44,7 +44,7 @@ def test_constants_match_header(lib):
     assert int(re.search(r"#define ATTN_ABI_VERSION (\d+)", text).group(1)) == lib.attn_abi_version()
     assert "(1 << 22)" in text and attn.ATTN_MAX_N == 1 << 22
     for name, val in (("ATTN_OK", 0), ("ATTN_ERR_INVALID_ARG", 1), ("ATTN_ERR_UNSUPPORTED", 2),
-                      ("ATTN_ERR_LAUNCH", 3)):
+                      ("ATTN_ERR_LAUNCH", 3), ("ATTN_ERR_NO_SCRATCH", 4)):
         assert re.search(rf"{name} = {val}\b", text)
         assert getattr(attn, name) == val
 
@@ -54,6 +54,7 @@ def test_status_strings_and_variants(lib):
     assert attn.attn_status_string(1) == "invalid argument"
     assert attn.attn_status_string(2) == "unsupported problem"
     assert attn.attn_status_string(3) == "kernel launch failed"
+    assert attn.attn_status_string(4) == "problem exceeds the allocation-free scratch"
     assert attn.attn_status_string(99) == "unknown status"
     n = attn.attn_num_variants()
     assert n >= 2
@@ -233,6 +234,46 @@ def test_decode_empty_problem_is_ok_and_launches_nothing(lib, kw):
     a = dict(DEC_GOOD)
     a.update(kw)
     assert attn.attn_decode_paged(**a) == attn.ATTN_OK
+
+
+NOALLOC_GOOD = {k: v for k, v in DEC_GOOD.items() if k != "workspace"}
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(lse=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(T=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(d=96), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(T=9), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(o=P + 8), attn.ATTN_ERR_UNSUPPORTED),
+    # 64 sequences x 8 KV heads x 32 columns of a 128k cache: 67.6 MB of
+    # partials, more than the 32 MiB scratch
+    (dict(B=8, Hq=256, Hkv=8, T=1, page_size=64, max_pages_per_seq=2048, num_pages=16384,
+          max_seq_len=131072), attn.ATTN_ERR_NO_SCRATCH),
+])
+def test_decode_noalloc_rejects_without_launching(lib, kw, expect):
+    a = dict(NOALLOC_GOOD)
+    a.update(kw)
+    assert attn.attn_decode_paged_noalloc(**a) == expect
+
+
+def test_decode_noalloc_scratch_limit_is_the_header_constant(lib):
+    text = open(HEADER).read()
+    assert "#define ATTN_DECODE_NOALLOC_MAX_BYTES ((size_t)32 << 20)" in text
+    assert attn.ATTN_DECODE_NOALLOC_MAX_BYTES == 32 << 20
+    big = attn.attn_decode_workspace_size(8, 256, 8, 1, 128, 64, 131072)
+    assert big > attn.ATTN_DECODE_NOALLOC_MAX_BYTES
+    # the decode workloads all fit
+    for args in ((8, 64, 8, 1, 128, 64, 131072, 0), (32, 32, 32, 1, 128, 16, 8192, 0),
+                 (8, 64, 8, 4, 128, 256, 131072, 4096)):
+        assert 0 < attn.attn_decode_workspace_size(*args) <= attn.ATTN_DECODE_NOALLOC_MAX_BYTES
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(max_seq_len=0)])
+def test_decode_noalloc_empty_problem_is_ok_and_launches_nothing(lib, kw):
+    a = dict(NOALLOC_GOOD)
+    a.update(kw)
+    assert attn.attn_decode_paged_noalloc(**a) == attn.ATTN_OK
 
 
 def test_decode_workspace_size(lib):
