@@ -60,6 +60,19 @@ def visible(i, j, causal=False, window=0, radius=0, n_global=0):
     return True
 
 
+def visible_block(i, j, causal=False, window=0, radius=0, n_global=0):
+    """The same rule over broadcast integer arrays of rows i and keys j."""
+    vis = np.ones(np.broadcast(i, j).shape, dtype=bool)
+    if causal:
+        vis &= j <= i
+    local = np.ones_like(vis)
+    if window > 0:
+        local &= j > i - window
+    if radius > 0:
+        local &= np.abs(i - j) <= radius
+    return vis & ((i < n_global) | (j < n_global) | local)
+
+
 def _candidate_keys(r0, r1, N, causal, window, radius, n_global):
     """Sorted key indices any row of [r0, r1) may see (a superset)."""
     if r0 < n_global:
@@ -111,17 +124,8 @@ def attention_general(q, k, v, scale, cu_seqlens, causal=False, window=0, radius
         for r0 in range(0, N, block):
             r1 = min(N, r0 + block)
             keys = _candidate_keys(r0, r1, N, causal, window, radius, n_global)
-            i = np.arange(r0, r1)[:, None]
-            j = keys[None, :]
-            vis = np.ones((r1 - r0, keys.size), dtype=bool)
-            if causal:
-                vis &= j <= i
-            local = np.ones_like(vis)
-            if window > 0:
-                local &= j > i - window
-            if radius > 0:
-                local &= np.abs(i - j) <= radius
-            vis &= (i < n_global) | (j < n_global) | local
+            vis = visible_block(np.arange(r0, r1)[:, None], keys[None, :], causal, window,
+                                radius, n_global)
             s = sigma * (qh[r0:r1] @ kh[keys].T)
             s = np.where(vis, s, -np.inf)
             m = s.max(axis=1, keepdims=True)
