@@ -10,7 +10,19 @@ FP8 oracle.
   at most 2^-4 * max|V| when the weights' errors share one sign; independent
   rounding errors leave about 2^-4 / sqrt(3) ~ 3.6 % of the output's own
   size.  Bar: max |err| <= 2^-4 * max|V| + 2^-7 * max|O|,
-  ||err||_2 <= 0.1 * ||O||_2.
+  ||err||_2 <= 0.1 * ||O||_2, and mean |err| <= 2^-4 / sqrt(3) * mean |O|:
+  with independent zero-mean roundings of relative size at most 2^-4 (the
+  kernel divides by the unrounded sum, so err = sum_j p_j eps_j v_j), the
+  rms error of an element is at most 2^-4 / sqrt(3) of the rms of the
+  weighted values, which on average over many rows is the output's own
+  size.  A window one key too wide or too narrow moves a row by about 1/w
+  of its weight, far above that.
+* Mask edges: closed forms with no weight rounding.  With Q = 0 every
+  score is 0 and every weight 2^4 (exact in e4m3), so O is the mean of the
+  visible dequantised V rows up to the final bf16 rounding and the fp8
+  product's block-sum error (below), and lse = ln(count); with window 1
+  each row sees only its own key, so O is that dequantised V row (exact in
+  bf16) and lse the diagonal score.
 * lse is summed from the unrounded weights, so its error is the scores'
   error.  The fp8 matrix product sums its 64-term blocks with an error of
   up to about 2^-13 of the sum of the terms' magnitudes (measured on this
@@ -85,9 +97,12 @@ def check_attention(o, lse, o_ref, l_ref, vmax, lbound, label):
     el = np.abs(lse.double().numpy() - l_ref)
     fro = np.sqrt((e * e).sum() / (o_ref * o_ref).sum())
     bound = 2.0 ** -4 * vmax + 2.0 ** -7 * np.abs(o_ref).max()
+    mean_bound = 2.0 ** -4 / math.sqrt(3.0) * np.abs(o_ref).mean()
     say(f"  {label}: max|err|={e.max():.3e} (bound {bound:.3e}) fro ratio {fro:.3e} "
+        f"mean|err|={e.mean():.3e} (bound {mean_bound:.3e}) "
         f"max|dlse|={el.max():.3e} (max ratio to bound {(el / lbound).max():.2f})")
     assert e.max() <= bound and fro <= 0.1 and np.all(el <= lbound), label
+    assert e.mean() <= mean_bound, label
 
 
 SHAPES = [
@@ -153,6 +168,66 @@ def test_fp8_one_hot_rows_return_the_value_row():
     _, sv, vdeq = F.quantize(to_f64(v))
     want = vdeq[0, 0, pick]
     np.testing.assert_allclose(to_f64(o.cpu())[0, 0], want, rtol=2 ** -7, atol=1e-6)
+
+
+EDGE_CASES = [(False, 0), (True, 0), (True, 1), (True, 63), (True, 64), (True, 65), (True, 100)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal,window", EDGE_CASES, ids=[f"c{c}w{w}" for c, w in EDGE_CASES])
+def test_fp8_q_zero_is_the_mean_of_the_visible_rows(causal, window, d):
+    """Q = 0: O_i is the mean of the dequantised V rows row i sees, which
+    are keys max(0, i - w + 1) .. i (causal window), 0 .. i (causal) or all
+    (non-causal); lse_i is ln of their number."""
+    B, Hq, Hkv, N = 1, 4, 2, 300
+    say(f"case fp8 Q=0 causal={causal} window={window} d={d}")
+    _, k, v = make_qkv(B, Hq, Hkv, N, d, seed=54 + window)
+    q = torch.zeros((B, Hq, N, d), dtype=torch.bfloat16)
+    _, _, _, _, dev = quantize_gpu(q, k, v)
+    o, lse = attn.fwd_fp8(*dev, causal=causal, window=window, scale=0.125)
+    torch.cuda.synchronize()
+    o, lse = to_f64(o.cpu()), lse.cpu().double().numpy()
+    _, _, vdeq = F.quantize(to_f64(v))
+    want = np.zeros((B, Hq, N, d))
+    mag = np.zeros((B, Hq, N, d))
+    count = np.zeros(N)
+    for i in range(N):
+        lo = max(0, i - window + 1) if window > 0 else 0
+        hi = i + 1 if causal else N
+        count[i] = hi - lo
+        for h in range(Hq):
+            want[0, h, i] = vdeq[0, h // (Hq // Hkv), lo:hi].mean(0)
+            mag[0, h, i] = np.abs(vdeq[0, h // (Hq // Hkv), lo:hi]).mean(0)
+    err = np.abs(o - want)
+    # bf16 rounding of the result, plus the fp8 product's block sums (about
+    # 2^-13 of the sum of the terms' magnitudes, taken with a factor 2)
+    bound = 2.0 ** -8 * np.abs(want) + 2.0 ** -12 * mag + 1e-6
+    say(f"  max|err| {err.max():.3e}, max ratio to bound {(err / bound).max():.3f}, "
+        f"max|dlse| {np.abs(lse - np.log(count)).max():.3e}")
+    assert np.all(err <= bound)
+    assert np.all(np.abs(lse - np.log(count)[None, None]) <= 1e-5)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_window_one_returns_the_own_value_row(d):
+    B, Hq, Hkv, N = 2, 4, 1, 200
+    say(f"case fp8 window=1 d={d}")
+    q, k, v = make_qkv(B, Hq, Hkv, N, d, seed=55)
+    _, _, _, _, dev = quantize_gpu(q, k, v)
+    sigma = 1 / math.sqrt(d)
+    o, lse = attn.fwd_fp8(*dev, causal=True, window=1, scale=sigma)
+    torch.cuda.synchronize()
+    _, _, dq = F.quantize(to_f64(q))
+    _, _, dk = F.quantize(to_f64(k))
+    _, _, dv = F.quantize(to_f64(v))
+    G = Hq // Hkv
+    own_v = np.repeat(dv, G, axis=1)
+    assert np.array_equal(to_f64(o.cpu()), own_v)
+    diag = float(np.float32(sigma)) * (dq * np.repeat(dk, G, axis=1)).sum(-1)
+    el = np.abs(lse.cpu().double().numpy() - diag)
+    lb = lse_bound(dq, dk, sigma, Hq, Hkv)
+    say(f"  max|dlse| {el.max():.3e} (max ratio to bound {(el / lb).max():.2f})")
+    assert np.all(el <= lb)
 
 
 @pytest.mark.parametrize("name", ["c2_causal_mha", "c4_causal_gqa"])
