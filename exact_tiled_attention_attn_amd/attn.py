@@ -27,7 +27,7 @@ EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_fwd_fp8", "attn_
             "attn_fp8_vt_bytes", "attn_bwd", "attn_bwd_workspace_size",
             "attn_decode_paged", "attn_decode_workspace_size", "attn_decode_paged_noalloc",
             "attn_num_variants",
-            "attn_variant_name", "attn_status_string", "attn_abi_version")
+            "attn_variant_name", "attn_status_string", "attn_device_info", "attn_abi_version")
 
 
 class AttnError(RuntimeError):
@@ -79,6 +79,8 @@ def load_library():
     lib.attn_variant_name.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_device_info.argtypes = [i] + [ctypes.POINTER(i)] * 4
+    lib.attn_device_info.restype = i
     lib.attn_abi_version.argtypes = []
     lib.attn_abi_version.restype = i
     _lib = lib
@@ -236,6 +238,15 @@ def attn_variant_name(variant):
 
 def attn_status_string(status):
     return load_library().attn_status_string(int(status)).decode()
+
+
+def attn_device_info(device=0):
+    """(compute units, peak engine clock kHz, memory clock kHz, bus bits)."""
+    vals = [ctypes.c_int(0) for _ in range(4)]
+    st = load_library().attn_device_info(int(device), *[ctypes.byref(x) for x in vals])
+    if st != ATTN_OK:
+        raise AttnError(f"attn_device_info: {attn_status_string(st)}", st)
+    return tuple(x.value for x in vals)
 
 
 def attn_abi_version():

@@ -79,7 +79,7 @@ attn_status_t validate_decode(const attn::DecodeProblem &p, bool need_workspace 
   if (!std::isfinite(p.scale)) return ATTN_ERR_INVALID_ARG;
   if (p.d != 64 && p.d != 128) return ATTN_ERR_UNSUPPORTED;
   if (!pow2_in(p.page_size, 16, 4096)) return ATTN_ERR_UNSUPPORTED;
-  if (static_cast<int64_t>(p.Hq / p.Hkv) * p.T > 32) return ATTN_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(p.Hq / p.Hkv) * p.T > 1024) return ATTN_ERR_UNSUPPORTED;
   if (p.max_seq_len > ATTN_MAX_N) return ATTN_ERR_UNSUPPORTED;
   if (p.B == 0 || p.max_seq_len == 0) return ATTN_OK;  // nothing to read or write
   if (!p.q || !p.k_cache || !p.v_cache || !p.block_table || !p.seq_lens || !p.o || !p.lse ||
@@ -259,6 +259,26 @@ const char *attn_status_string(attn_status_t status) {
     case ATTN_ERR_NO_SCRATCH: return "problem exceeds the allocation-free scratch";
   }
   return "unknown status";
+}
+
+attn_status_t attn_device_info(int device, int *num_cus, int *max_clock_khz, int *mem_clock_khz,
+                               int *mem_bus_bits) {
+  if (device < 0) return ATTN_ERR_INVALID_ARG;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess) return ATTN_ERR_LAUNCH;
+  if (device >= n) return ATTN_ERR_INVALID_ARG;
+  const struct {
+    int *out;
+    hipDeviceAttribute_t attr;
+  } q[] = {{num_cus, hipDeviceAttributeMultiprocessorCount},
+           {max_clock_khz, hipDeviceAttributeClockRate},
+           {mem_clock_khz, hipDeviceAttributeMemoryClockRate},
+           {mem_bus_bits, hipDeviceAttributeMemoryBusWidth}};
+  for (const auto &e : q) {
+    if (!e.out) continue;
+    if (hipDeviceGetAttribute(e.out, e.attr, device) != hipSuccess) return ATTN_ERR_LAUNCH;
+  }
+  return ATTN_OK;
 }
 
 int attn_abi_version(void) { return ATTN_ABI_VERSION; }

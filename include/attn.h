@@ -241,12 +241,13 @@ size_t attn_bwd_workspace_size(int B, int Hq, int N);
  *   page_size    a power of two in [16, 4096]
  *   max_seq_len  host-side upper bound of seq_lens (decides the key split)
  *   scale        as for attn_fwd; window <= 0: none
- * Requires (Hq / Hkv) * T <= 32 (the query heads of one KV head times the
- * new tokens fill one matrix-core column block).  Keys are split into
+ * Requires (Hq / Hkv) * T <= 1024 (the query heads of one KV head times the
+ * new tokens, processed in blocks of 32 matrix-core columns that share each
+ * K/V tile through the cache).  Keys are split into
  * ranges processed by separate workgroups; the partial results are merged
  * with lse = ln sum_s exp(lse_s), o = sum_s exp(lse_s - lse) o_s.  Two
  * kernels are enqueued on `stream`.  Errors as for attn_fwd (also: T < 1,
- * page size, heads x tokens > 32, unaligned table or lens -> codes as
+ * page size, heads x tokens > 1024, unaligned table or lens -> codes as
  * listed); B == 0 or max_seq_len == 0 launches nothing. */
 attn_status_t attn_decode_paged(const void *q, const void *k_cache, const void *v_cache,
                                 const int *block_table, const int *seq_lens, void *o, float *lse,
@@ -290,8 +291,18 @@ const char *attn_variant_name(int variant);
 /* Static, human-readable text for a status code. */
 const char *attn_status_string(attn_status_t status);
 
+/* What the HIP runtime reports for device `device`, for callers that build
+ * a roofline denominator on the machine they run on (matrix-core peak =
+ * compute units x peak engine clock x FLOP per CU and clock): compute units,
+ * peak engine clock in kHz, memory clock in kHz and memory bus width in
+ * bits.  A null pointer skips that field.  ATTN_ERR_INVALID_ARG for a device
+ * id out of range, ATTN_ERR_LAUNCH when a runtime query fails; launches
+ * nothing and leaves the current device unchanged. */
+attn_status_t attn_device_info(int device, int *num_cus, int *max_clock_khz, int *mem_clock_khz,
+                               int *mem_bus_bits);
+
 /* ABI version of this header (incremented on any signature change). */
-#define ATTN_ABI_VERSION 6
+#define ATTN_ABI_VERSION 7
 int attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -49,6 +49,15 @@ def test_constants_match_header(lib):
         assert getattr(attn, name) == val
 
 
+def test_device_info_rejects_a_negative_device(lib):
+    import ctypes
+    x = ctypes.c_int(-5)
+    assert lib.attn_device_info(-1, ctypes.byref(x), None, None, None) == attn.ATTN_ERR_INVALID_ARG
+    assert x.value == -5
+    with pytest.raises(attn.AttnError):
+        attn.attn_device_info(-1)
+
+
 def test_status_strings_and_variants(lib):
     assert attn.attn_status_string(0) == "ok"
     assert attn.attn_status_string(1) == "invalid argument"
@@ -216,7 +225,7 @@ DEC_GOOD = dict(q=P, k_cache=P, v_cache=P, block_table=P, seq_lens=P, o=P, lse=P
     (dict(page_size=24), attn.ATTN_ERR_UNSUPPORTED),     # not a power of two
     (dict(page_size=8), attn.ATTN_ERR_UNSUPPORTED),
     (dict(page_size=8192), attn.ATTN_ERR_UNSUPPORTED),
-    (dict(T=9), attn.ATTN_ERR_UNSUPPORTED),              # 4 heads x 9 tokens > 32
+    (dict(T=257), attn.ATTN_ERR_UNSUPPORTED),            # 4 heads x 257 tokens > 1024
     (dict(block_table=P + 2), attn.ATTN_ERR_UNSUPPORTED),
     (dict(o=P + 8), attn.ATTN_ERR_UNSUPPORTED),
     (dict(max_seq_len=(1 << 22) + 1), attn.ATTN_ERR_UNSUPPORTED),
@@ -244,7 +253,7 @@ NOALLOC_GOOD = {k: v for k, v in DEC_GOOD.items() if k != "workspace"}
     (dict(lse=0), attn.ATTN_ERR_INVALID_ARG),
     (dict(T=0), attn.ATTN_ERR_INVALID_ARG),
     (dict(d=96), attn.ATTN_ERR_UNSUPPORTED),
-    (dict(T=9), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(T=257), attn.ATTN_ERR_UNSUPPORTED),
     (dict(o=P + 8), attn.ATTN_ERR_UNSUPPORTED),
     # 64 sequences x 8 KV heads x 32 columns of a 128k cache: 67.6 MB of
     # partials, more than the 32 MiB scratch
