@@ -11,9 +11,13 @@
 // h / (Hq / Hkv).
 //
 // Schedule (split-KV): one single-wave workgroup per (sequence, KV head,
-// key range of `chunk` keys).  The G query heads x T tokens of the KV group
-// are the wave's (at most 32) MFMA columns, so every cached K/V byte is read
-// from HBM once for all the heads that share it.  32-key tiles are gathered
+// key range of `chunk` keys, block of 32 columns).  The G query heads x T
+// tokens of the KV group are the MFMA columns, 32 per wave, so every cached
+// K/V byte is read from HBM once for all the heads that share it; with more
+// than 32 columns (multi-query attention at real head counts, several new
+// tokens) the column blocks of one key range run on one XCD, one after the
+// other in dispatch order, and all but the first find the K/V tiles in that
+// XCD's L2.  32-key tiles are gathered
 // through the page table (two 16-row groups per tile, each inside one page)
 // and staged two tiles ahead through registers into the wave's LDS tile.
 // Per tile: S^T = K Q^T (8 MFMA), running max / sum per column, O^T += V^T
@@ -55,7 +59,8 @@ struct DecParams {
   float *lse;                   // [B][Hq][T]
   float *part_o;                // [B][Hkv][nsplit][ncols][D]
   float *part_lse;              // [B][Hkv][nsplit][ncols]
-  int B, Hq, Hkv, G, T, ncols;  // ncols = G * T <= 32
+  int B, Hq, Hkv, G, T, ncols;  // ncols = G * T
+  int ncb, nwork;               // 32-column blocks; (sequence, split, KV head) items
   int ps, ps_shift;             // page size (power of two)
   int num_pages, max_pages;
   int nsplit, chunk;            // keys per split: multiple of unit
@@ -136,19 +141,25 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(DecParams prm) {
 
   const int lane = threadIdx.x;
   const int l32 = lane & 31, hh = lane >> 5;
-  // blockIdx.x = (b * nsplit + split) * Hkv + kvh: the Hkv workgroups that
+  // work item w = (b * nsplit + split) * Hkv + kvh: the Hkv workgroups that
   // read the same cache pages (token rows hold every KV head) run together,
   // so each page is streamed from HBM in one pass rather than in Hkv
-  // scattered 256-byte pieces
-  const int kvh = blockIdx.x % prm.Hkv;
-  const int bs = blockIdx.x / prm.Hkv;
+  // scattered 256-byte pieces.  Column block cb of item w is workgroup
+  // 8 (ncb (w / 8) + cb) + w % 8: the same XCD (workgroups go to the 8 XCDs
+  // in turn) and 8 ids after block cb - 1.  With one block, w = blockIdx.x.
+  const int u = blockIdx.x;
+  const int cb = (u >> 3) % prm.ncb;
+  const int w = ((u >> 3) / prm.ncb) * 8 + (u & 7);
+  if (w >= prm.nwork) return;  // padding of the last group of 8 items
+  const int kvh = w % prm.Hkv;
+  const int bs = w / prm.Hkv;
   const int split = bs % prm.nsplit, b = bs / prm.nsplit;
   const int bk = b * prm.Hkv + kvh;
   const int L = prm.lens[b];
   const int T = prm.T;
 
   // this lane's column: query head kvh * G + g, token t
-  const int col = l32;
+  const int col = 32 * cb + l32;
   const bool col_ok = col < prm.ncols;
   const int g = col_ok ? col / T : 0, t = col_ok ? col % T : 0;
   const int pos = L - T + t;                   // position of the query token
@@ -357,6 +368,7 @@ hipError_t launch_decode_d(const DecodeProblem &p, const DecodePlan &plan, hipSt
   prm.part_lse = prm.part_o + plan.part_o_floats;
   prm.B = p.B; prm.Hq = p.Hq; prm.Hkv = p.Hkv; prm.G = p.Hq / p.Hkv; prm.T = p.T;
   prm.ncols = prm.G * p.T;
+  prm.ncb = (prm.ncols + 31) / 32;
   prm.ps = p.page_size;
   prm.ps_shift = __builtin_ctz((unsigned)p.page_size);
   prm.num_pages = p.num_pages;
@@ -369,16 +381,20 @@ hipError_t launch_decode_d(const DecodeProblem &p, const DecodePlan &plan, hipSt
   prm.neg = p.scale < 0.0f ? 1 : 0;
   prm.window = p.window;
   const long long groups = (long long)p.B * p.Hkv;
-  const long long wgs = groups * plan.nsplit;
+  const long long items = groups * plan.nsplit;
+  const long long wgs = prm.ncb == 1 ? items : (items + 7) / 8 * 8 * prm.ncb;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
+  prm.nwork = (int)items;
   void *args[] = {&prm};
   // K/V bytes the call may read (every split full): a working set that fits
   // the 256 MB last-level cache can stay there from one call to the next
   // and is read with ordinary loads; a larger one is streamed with
   // nontemporal loads (measured: 7-10 % faster at 1.9 GB, 9 % slower at
   // 135 MB, where ordinary loads hit the last-level cache).
+  // Column blocks after the first read their K/V tiles from L2, which a
+  // nontemporal load would not have kept: those calls use ordinary loads.
   const double kv_bytes = (double)groups * plan.nsplit * plan.chunk * D * 4.0;
-  const void *split = kv_bytes > kLastLevelCacheBytes
+  const void *split = kv_bytes > kLastLevelCacheBytes && prm.ncb == 1
                           ? reinterpret_cast<const void *>(&attn_decode_split_kernel<D, 2>)
                           : reinterpret_cast<const void *>(&attn_decode_split_kernel<D, 0>);
   hipError_t e = hipLaunchKernel(split, dim3((unsigned)wgs), dim3(64), args, 0, stream);
@@ -407,8 +423,11 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int T, int d, int page_size, int 
   // splits empty, so a typical call runs in a few rounds of workgroups.
   // (Measured on 8 sequences of 12k..102k keys: 3072-4096 in total is 3 %
   // faster than 8192 and 13 % faster than 2048.)
+  // With more than 32 columns each key range is one workgroup per 32-column
+  // block, so the count is of (range, block) pairs.
+  const long long ncb = ((long long)(Hq / Hkv) * T + 31) / 32;
   const long long groups = (long long)B * Hkv;
-  long long want = (4096 + groups - 1) / groups;
+  long long want = (4096 + groups * ncb - 1) / (groups * ncb);
   long long chunk = (span + want - 1) / want;
   chunk = (chunk + unit - 1) / unit * unit;
   if (chunk < unit) chunk = unit;

@@ -138,6 +138,11 @@ DECODE_WORKLOADS = {
     "d2_decode_mha_8k": DecodeWorkload("d2_decode_mha_8k", 32, 32, 32, 1, 128, 16, 8192, 22),
     "d3_decode_window_spec4": DecodeWorkload("d3_decode_window_spec4", 8, 64, 8, 4, 128, 256,
                                              131072, 23, window=4096),
+    # multi-query: one KV head for 64 query heads (64 columns per KV head)
+    "d4_decode_mqa_128k": DecodeWorkload("d4_decode_mqa_128k", 8, 64, 1, 1, 128, 64, 131072, 24),
+    # 16 query heads per KV head x 4 new tokens (64 columns per KV head)
+    "d5_decode_gqa16_spec4": DecodeWorkload("d5_decode_gqa16_spec4", 8, 32, 2, 4, 128, 64,
+                                            131072, 25),
 }
 
 

@@ -76,6 +76,14 @@ CASES = [
     (2, 32, 4, 4, 128, 64, [70000, 3], 4096),
     (1, 17, 1, 1, 128, 32, [333], 0),                 # 17 columns: the 32-column kernel
     (2, 12, 2, 3, 64, 16, [50, 401], 0),              # 18 columns at d = 64
+    # more than 32 columns: blocks of 32 columns per key range
+    (2, 64, 1, 1, 128, 64, [3000, 700], 0),           # multi-query, 64 heads
+    (2, 32, 2, 4, 128, 16, [1200, 65], 0),            # 16 heads x 4 tokens
+    (1, 40, 1, 1, 64, 16, [500], 0),                  # 40 columns: ragged second block
+    (2, 16, 1, 5, 128, 32, [900, 3], 300),            # 80 columns, window, T > L
+    (3, 96, 3, 3, 128, 256, [5000, 129, 1], 64),      # 96 columns, window
+    (1, 128, 1, 8, 128, 64, [2000], 0),               # 1024 columns, the limit
+    (9, 64, 1, 1, 128, 16, [40] * 9, 0),              # 9 items: padding of the last 8
 ]
 
 
