@@ -37,12 +37,17 @@ MAIN = "c2_causal_mha"
 OTHERS = ["c2_causal_mha_sharp", "c3_causal_window", "c4_causal_gqa", "c5_long_causal",
           "c5_long_window"]
 BWD_OTHERS = ["c4_causal_gqa"]
-DECODE = ["d1_decode_gqa_128k", "d2_decode_mha_8k", "d3_decode_window_spec4"]
+DECODE = ["d1_decode_gqa_128k", "d2_decode_mha_8k", "d3_decode_window_spec4",
+          "d4_decode_mqa_128k", "d5_decode_gqa16_spec4"]
 VARLEN = ["v1_packed_causal_gqa", "l1_longformer_4k"]
 FP8_OTHERS = ["c4_causal_gqa", "c5_long_causal"]
-KERNEL_SRC = os.path.join(ROOT, "exact_tiled_attention_attn_amd", "csrc", "attn_fwd.hip")
-# the forward kernel also compiles the shared device helpers
-KERNEL_HEADERS = [os.path.join(ROOT, "exact_tiled_attention_attn_amd", "csrc", "attn_device.h")]
+CSRC = os.path.join(ROOT, "exact_tiled_attention_attn_amd", "csrc")
+KERNEL_SRC = os.path.join(CSRC, "attn_fwd.hip")
+# source of each kind of kernel the line times (the forward's also serves the
+# packed-sequence forward); every kernel also compiles the shared device helpers
+KERNEL_SOURCES = {"fwd": "attn_fwd.hip", "varlen": "attn_fwd.hip", "bwd": "attn_bwd.hip",
+                  "fp8": "attn_fp8.hip", "decode": "attn_decode.hip"}
+KERNEL_HEADERS = [os.path.join(CSRC, "attn_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -50,14 +55,16 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_sha() -> str:
-    """sha256[:16] of the forward kernel's code: its source and the device
-    header it includes, with // comments, trailing blanks and empty lines
-    removed, and the device compile flags.  A comment edit keeps stored
-    counter data valid; any change to the code or the flags invalidates it."""
+def kernel_sha(kind: str = "fwd") -> str:
+    """sha256[:16] of one kind of kernel's code (KERNEL_SOURCES; the forward's
+    is KERNEL_SRC): its source and the device header it includes, with //
+    comments, trailing blanks and empty lines removed, and the device compile
+    flags.  A comment edit keeps stored counter data valid; any change to the
+    code or the flags invalidates it."""
     from exact_tiled_attention_attn_amd.build import DEVICE_ONLY, COMMON
+    src = KERNEL_SRC if kind == "fwd" else os.path.join(CSRC, KERNEL_SOURCES[kind])
     code = []
-    for path in [KERNEL_SRC] + KERNEL_HEADERS:
+    for path in [src] + KERNEL_HEADERS:
         with open(path) as f:
             for line in f:
                 line = line.split("//", 1)[0].rstrip()
@@ -310,18 +317,52 @@ def _cpu_model():
     return platform.processor()
 
 
-def traffic_for(workload, sha):
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel source; else None."""
+def fwd_key(name, variant):
+    """traffic.json key of a forward workload under a kernel variant."""
+    return name if variant == 0 else f"{name}@v{variant}"
+
+
+def traffic_for(key, sha):
+    """HBM bytes per call from the committed counter summary (entry `key`:
+    a forward workload's name, or "bwd:", "fp8:", "varlen:", "decode:" and
+    the workload's name), if they were taken on the current source of that
+    kernel (`sha`); else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    e = t.get("workloads", {}).get(workload)
-    if not e or t.get("kernel_source_sha") != sha:
+    e = t.get("workloads", {}).get(key)
+    if not e or e.get("kernel_source_sha") != sha:
         return None
-    return e.get("hbm_bytes_per_launch")
+    return e.get("hbm_bytes_per_call")
+
+
+# Dense matrix-core FLOP per compute unit and clock: v_mfma_f32_32x32x16_bf16
+# does 32 x 32 x 16 multiply-adds (32 768 FLOP) and issues every 32 clocks on
+# each of a CU's 4 SIMDs (32.0 busy cycles per MFMA in the counters); the
+# dense fp8 rate is twice that (the published fp8 and bf16 peaks are 2 : 1).
+BF16_FLOP_PER_CU_CLK = 32 * 32 * 16 * 2 // 32 * 4
+FP8_FLOP_PER_CU_CLK = 2 * BF16_FLOP_PER_CU_CLK
+
+
+def derive_peaks(info, published_bf16, published_fp8):
+    """Peak dense MFMA rates of the device bench.py runs on, from what the HIP
+    runtime reports (compute units, peak engine clock) and the FLOP per CU
+    and clock above, with the published figures beside them."""
+    cus, clock_khz, mem_khz, bus_bits = info
+    if cus <= 0 or clock_khz <= 0:
+        raise RuntimeError(f"device reports {cus} CUs at {clock_khz} kHz")
+    bf16 = cus * clock_khz * 1e3 * BF16_FLOP_PER_CU_CLK / 1e12
+    return {"bf16_tflops": round(bf16, 1),
+            "fp8_tflops": round(bf16 * FP8_FLOP_PER_CU_CLK / BF16_FLOP_PER_CU_CLK, 1),
+            "cus": cus, "max_clock_mhz": clock_khz / 1e3,
+            "bf16_flop_per_cu_clock": BF16_FLOP_PER_CU_CLK,
+            "fp8_flop_per_cu_clock": FP8_FLOP_PER_CU_CLK,
+            "source": "hipDeviceAttributeMultiprocessorCount x hipDeviceAttributeClockRate x "
+                      "FLOP/CU/clock of v_mfma_f32_32x32x16_bf16 (fp8: twice that)",
+            "published_bf16_tflops": published_bf16, "published_fp8_tflops": published_fp8,
+            "memory_clock_mhz": mem_khz / 1e3, "memory_bus_bits": bus_bits}
 
 
 def main():
@@ -338,6 +379,9 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward timing")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed-sequence / structured-mask timing")
+    ap.add_argument("--varlen-case", default=None,
+                    help="time only this packed-sequence / structured-mask workload")
+    ap.add_argument("--decode-case", default=None, help="time only this paged-decode workload")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
@@ -361,7 +405,9 @@ def main():
         sys.exit(2)
     attn.load_library()
     props = torch.cuda.get_device_properties(0)
-    peak = MI355X_BF16_DENSE_TFLOPS
+    peaks = derive_peaks(attn.attn_device_info(0), MI355X_BF16_DENSE_TFLOPS,
+                         MI355X_FP8_DENSE_TFLOPS)
+    peak, fp8_peak = peaks["bf16_tflops"], peaks["fp8_tflops"]
 
     if args.copy_calibration:
         n = 1 << 30
@@ -402,7 +448,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": traffic_for(w.name, sha),
+            "traffic": traffic_for(fwd_key(w.name, args.variant), sha),
             "kernel": "attn_fwd_kernel",
             "avg_launch_ms": round(ev_ms, 4),
             "flops_per_launch": f,
@@ -410,6 +456,7 @@ def main():
         },
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},
+        "peak_derivation": peaks,
         "kernel_source_sha": sha,
     }
     if not args.no_others:
@@ -423,7 +470,9 @@ def main():
             of = flops(ow)
             others[name] = {"tflops": round(of / (em * 1e-3) / 1e12, 2),
                             "pct_of_peak": round(100 * of / (em * 1e-3) / 1e12 / peak, 2),
-                            "ms": round(em, 4), "steps": steps}
+                            "ms": round(em, 4), "steps": steps,
+                            "traffic": traffic_for(fwd_key(name, args.variant), sha),
+                            "algorithmic_bytes": algorithmic_bytes(ow)}
             torch.cuda.empty_cache()
         out["other_workloads"] = others
     if not args.no_bwd:
@@ -436,7 +485,8 @@ def main():
             bf = bwd_flops(bwl)
             bw[name] = {"tflops": round(bf / (em * 1e-3) / 1e12, 2),
                         "pct_of_peak": round(100 * bf / (em * 1e-3) / 1e12 / peak, 2),
-                        "ms": round(em, 4), "flops_per_call": bf}
+                        "ms": round(em, 4), "flops_per_call": bf,
+                        "traffic": traffic_for("bwd:" + name, kernel_sha("bwd"))}
             torch.cuda.empty_cache()
         out["backward"] = bw
     if not args.no_fp8:
@@ -447,33 +497,38 @@ def main():
             em, qm = time_fp8(fw, args.steps, max(1, args.warmup // 2), torch, attn)
             ff = flops(fw)
             f8[name] = {"tflops": round(ff / (em * 1e-3) / 1e12, 2),
-                        "pct_of_fp8_peak": round(100 * ff / (em * 1e-3) / 1e12
-                                                 / MI355X_FP8_DENSE_TFLOPS, 2),
-                        "ms": round(em, 4), "quantize_ms": round(qm, 4)}
+                        "pct_of_fp8_peak": round(100 * ff / (em * 1e-3) / 1e12 / fp8_peak,
+                                                 2),
+                        "ms": round(em, 4), "quantize_ms": round(qm, 4),
+                        "traffic": traffic_for("fp8:" + name, kernel_sha("fp8"))}
             torch.cuda.empty_cache()
         out["fp8"] = f8
     if not args.no_varlen:
         var = {}
-        for name in VARLEN if not args.no_others else VARLEN[:1]:
+        for name in ([args.varlen_case] if args.varlen_case else
+                     VARLEN if not args.no_others else VARLEN[:1]):
             vw = VARLEN_WORKLOADS[name]
             log(f"timing varlen {name}")
             em = time_varlen(vw, args.steps, max(1, args.warmup // 2), torch, attn)
             vf = varlen_flops(vw)
             var[name] = {"tflops": round(vf / (em * 1e-3) / 1e12, 2),
                          "pct_of_peak": round(100 * vf / (em * 1e-3) / 1e12 / peak, 2),
-                         "ms": round(em, 4), "flops_per_call": vf}
+                         "ms": round(em, 4), "flops_per_call": vf,
+                         "traffic": traffic_for("varlen:" + name, kernel_sha("varlen"))}
             torch.cuda.empty_cache()
         out["varlen"] = var
     if not args.no_decode:
         dec = {}
-        for name in DECODE if not args.no_others else DECODE[:1]:
+        for name in ([args.decode_case] if args.decode_case else
+                     DECODE if not args.no_others else DECODE[:1]):
             dw = DECODE_WORKLOADS[name]
             log(f"timing decode {name}")
             em, lens = time_decode(dw, args.steps, max(1, args.warmup // 2), torch, attn)
             nb = decode_bytes(dw, lens)
             dec[name] = {"GB/s": round(nb / (em * 1e-3) / 1e9, 1),
                          "frac_of_hbm_peak": round(nb / (em * 1e-3) / 1e9 / MI355X_HBM_GBPS, 4),
-                         "ms": round(em, 4), "bytes_per_call": nb, "seq_lens": lens}
+                         "ms": round(em, 4), "bytes_per_call": nb, "seq_lens": lens,
+                         "traffic": traffic_for("decode:" + name, kernel_sha("decode"))}
             torch.cuda.empty_cache()
         out["decode"] = dec
     if not args.no_cpu:

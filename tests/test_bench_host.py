@@ -52,22 +52,51 @@ def test_kernel_sha_covers_the_device_header_and_flags(tmp_path, monkeypatch):
 
 def test_traffic_only_for_the_source_it_was_taken_on(tmp_path, monkeypatch):
     f = tmp_path / "traffic.json"
-    f.write_text(json.dumps({"kernel_source_sha": "abc",
-                             "workloads": {"w": {"hbm_bytes_per_launch": 123}}}))
+    f.write_text(json.dumps({"workloads": {"w": {"kernel_source_sha": "abc",
+                                                 "hbm_bytes_per_call": 123},
+                                           "bwd:w": {"kernel_source_sha": "def",
+                                                     "hbm_bytes_per_call": 456}}}))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
     assert bench.traffic_for("w", "abc") == 123
     assert bench.traffic_for("w", "abd") is None
+    assert bench.traffic_for("bwd:w", "def") == 456
+    assert bench.traffic_for("bwd:w", "abc") is None
     assert bench.traffic_for("other", "abc") is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
     assert bench.traffic_for("w", "abc") is None
 
 
-def test_committed_traffic_matches_the_current_kernel_source():
-    """The stored HBM counters are those of the kernel as it stands, so the
-    bench line's roofline.traffic is not null."""
+def test_forward_traffic_keys_name_the_variant():
+    assert bench.fwd_key("c2", 0) == "c2"
+    assert bench.fwd_key("c2", 2) == "c2@v2"
+
+
+def test_kernel_kinds_hash_their_own_source():
+    shas = {k: bench.kernel_sha(k) for k in bench.KERNEL_SOURCES}
+    assert shas["fwd"] == shas["varlen"] == bench.kernel_sha()
+    assert len({shas["fwd"], shas["bwd"], shas["fp8"], shas["decode"]}) == 4
+
+
+def test_committed_traffic_is_consistent():
+    """Each stored entry's bytes are its scaled counters; the main workload's
+    entry is that of the forward kernel as it stands, so the bench line's
+    roofline.traffic is not null."""
     with open(bench.TRAFFIC_FILE) as fh:
         t = json.load(fh)
-    assert t["kernel_source_sha"] == bench.kernel_sha()
-    e = t["workloads"]["c2_causal_mha"]
-    scaled = e["fetch_kib"] * 1024 * t["fetch_scale"] + e["write_kib"] * 1024 * t["write_scale"]
-    assert abs(scaled - e["hbm_bytes_per_launch"]) <= 1
+    for key, e in t["workloads"].items():
+        scaled = (e["fetch_kib"] * 1024 * t["fetch_scale"]
+                  + e["write_kib"] * 1024 * t["write_scale"])
+        assert abs(scaled - e["hbm_bytes_per_call"]) <= 1, key
+        kind = key.split(":", 1)[0] if ":" in key else "fwd"
+        assert kind in bench.KERNEL_SOURCES, key
+    assert t["workloads"][bench.MAIN]["kernel_source_sha"] == bench.kernel_sha()
+
+
+def test_peaks_from_device_properties():
+    p = bench.derive_peaks((256, 2400000, 2000000, 8192), 2516.6, 5033.2)
+    assert p["bf16_tflops"] == 2516.6 and p["fp8_tflops"] == 5033.2
+    assert p["bf16_flop_per_cu_clock"] == 4096 and p["max_clock_mhz"] == 2400.0
+    assert bench.derive_peaks((128, 2100000, 0, 0), 0, 0)["bf16_tflops"] == 1101.0
+    import pytest
+    with pytest.raises(RuntimeError):
+        bench.derive_peaks((0, 2400000, 0, 0), 0, 0)
