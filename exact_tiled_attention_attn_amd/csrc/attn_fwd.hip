@@ -106,6 +106,7 @@ struct Params {
   int radius;
   int nglob;
   int compact;    // sequence lengths differ: launch only non-empty tiles first
+  int slots;      // persistent launch: workgroups per XCD (0: one per tile)
 };
 
 template <int D>
@@ -281,10 +282,13 @@ __device__ __forceinline__ bool compact_slot(const Params &prm, int n, int &rank
 // kRows query rows per workgroup, P heads per workgroup (wave w serves head
 // w % P on rows (w / P) * 32 ..).  GEN: packed sequences [cu[b], cu[b+1]).
 template <int P, int kRows, bool GEN>
-__device__ __forceinline__ Task make_task(const Params &prm, int wave) {
+__device__ __forceinline__ Task make_task(const Params &prm, int wave, int pq = -1, int phgb = -1) {
   Task tk;
   int qrank, hgb;
-  if constexpr (GEN) {
+  if (!GEN && pq >= 0) {  // given by the persistent schedule
+    qrank = pq;
+    hgb = phgb;
+  } else if constexpr (GEN) {
     // packed sequences of different lengths: tile rank slowest, so the
     // heaviest tiles of every sequence go first and consecutive workgroups
     // (dealt round-robin to the XCDs) spread every sequence over all XCDs
@@ -724,6 +728,11 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D == 64) ? 3 : 2) void attn_fw
 // Staging: group A loads the K tiles, group B the V tiles, HBM -> LDS
 // directly (no registers), into rings of three K and four V slots; the
 // loads of a matrix phase are spread over its k-steps.
+//
+// Launch: one workgroup per query tile, or persistent (persistent_task):
+// one workgroup per CU that runs its share of the tiles one after another,
+// which saves the gap between one workgroup's end and the next one's start
+// on the CU (2-4 % on the 8k causal and the windowed workloads).
 // ---------------------------------------------------------------------------
 
 // Direct HBM -> LDS load of 16 bytes per lane (buffer_load ... lds): lane l
@@ -902,6 +911,37 @@ __device__ __forceinline__ void mfma_phase(const lchar *kb, const lchar *vb,
   if constexpr (DO_PV) lrnd += (rp[0] + rp[1]) + (rp[2] + rp[3]);
 }
 
+// Persistent schedule (one workgroup per CU, each running several tiles in
+// turn).  XCD x takes the head groups x, x + 8, ..., so every tile of a head
+// reads its K/V behind one L2.  Its tiles are dealt to its S slots in
+// rounds, alternately forwards and backwards, which evens out the causal
+// work: in round r slot s takes tile k = r S + s (r even) or r S + S - 1 - s
+// (r odd).  Tile k is, without a window, head k / nq, query tile rank
+// k % nq (head by head, heaviest first within a head: the slots running at
+// one time mostly share a head and stream the same K/V tiles from key 0
+// up); with a window, rank k / hx of head k % hx (the ranks running at one
+// time span fewer rows of each head, and so fewer keys).  Measured on
+// MI355X: each order is 2-4 % faster than the other where it is used.
+// Returns false when slot s has no tile in round r.
+__device__ __forceinline__ bool persistent_task(const Params &prm, int r, int &qrank, int &hgb) {
+  const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int H = prm.B * prm.groups;
+  const int hx = (H - x + 7) >> 3;  // head groups of XCD x
+  const int S = prm.slots;
+  const int k = r * S + ((r & 1) ? S - 1 - slot : slot);
+  if (k >= prm.nq * hx) return false;
+  int hl;
+  if (prm.window > 0) {
+    qrank = k / hx;
+    hl = k - qrank * hx;
+  } else {
+    hl = k / prm.nq;
+    qrank = k - hl * prm.nq;
+  }
+  hgb = hl * 8 + x;
+  return true;
+}
+
 template <int D, int P, bool GEN>
 __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(Params prm) {
   using g = Geo<D>;
@@ -920,183 +960,207 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(Params prm) {
   const int gt = tid & 255;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  const Task tk = make_task<P, kRows, GEN>(prm, wave);
-  if (tk.empty) return;  // the whole workgroup
-  const int N = tk.N;
-  const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(prm.k + tk.kv_slice * D, (uint32_t)N * D * 2);
-  const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(prm.v + tk.kv_slice * D, (uint32_t)N * D * 2);
-
-  bf16x8 qf[g::kKSteps];
-  load_q<D>(prm, tk, l32, hh, qf);
-  const int k_lane = k_lane_off<D>(lane);
-  const int v_lane = v_lane_off<D>(lane);
-
-  f32x16 oacc[g::kDB];
-#pragma unroll
-  for (int i = 0; i < g::kDB; ++i) oacc[i] = f32x16{};
-  RowState st;
-  const float c = prm.c;
-#pragma unroll
-  for (int kk = 0; kk < g::kKSteps; ++kk) asm volatile("" : "+v"(qf[kk]) : : "memory");
-
-  const int count = tk.wg.count();
-  auto row_of = [&](int k) { return k < count ? tk.wg.tile(k) * kBN : N; };
-  auto ktile = [&](int j) { return (lchar *)smem + (j % kKSlots) * dt::kRegionB; };
-  auto vtile = [&](int j) {
-    return (lchar *)smem + (kKSlots + (j & (kVSlots - 1))) * dt::kRegionB;
-  };
-  auto sees = [&](int m) { return m < count && tk.w.has(tk.wg.tile(m)); };
-
-  // S of two tiles in flight: S(m) in sb[m % 2] is turned into weights while
-  // the MFMAs of S(m + 1) run.
-  f32x16 sb[2][2];
-  bf16x8 pf[2][2];
-  bf16x8 ka[3][2];
-  bf16x8 va[4];
-
-  // Group A stages K, group B stages V.
-  auto group_program = [&](auto grp_c) {
-    constexpr int G = decltype(grp_c)::value;
-    const int w4 = wave & 3;
-    // Step m >= 1 reads K(m + 1) (half-steps 2m, group A, and 2m + 1, group
-    // B), step 0 reads K(0) and K(1); V(j) is read in half-steps 2j + 2 and
-    // 2j + 3.  A slot's next tile is loaded (straight into LDS) once both
-    // groups have read the previous one: group A loads K(m + 3) in its
-    // matrix phase of step m >= 1 (K(3) too in step 1) and waits for K(m + 2)
-    // at the end of its softmax phase; group B loads V(m + 2) in its matrix
-    // phase of step m and waits for V(m) at its end.  The loads are spread
-    // over the phase's k-steps.  Loads past the last tile read outside the
-    // buffer (zero, no memory access), so the number of loads in flight does
-    // not depend on the tile count.
-    const __amdgpu_buffer_rsrc_t rs = G == 0 ? rs_k : rs_v;
-    dt dma;
-    dma.init(G == 0 ? g::kCh + 1 : g::kCh + 4, w4, lane);
-    auto region = [&](int j) { return (uint32_t)(uintptr_t)(G == 0 ? ktile(j) : vtile(j)); };
-    if constexpr (G == 0) {
-      dma.issue(rs, region(0), row_of(0), w4);
-      dma.issue(rs, region(1), row_of(1), w4);
-      dma.issue(rs, region(2), row_of(2), w4);
-      wait_loads<dt::kWaveLoads>();
-    } else {
-      dma.issue(rs, region(0), row_of(0), w4);
-      dma.issue(rs, region(1), row_of(1), w4);
+  for (int r = 0;; ++r) {
+    int pq = -1, ph = -1;
+    if (GEN || prm.slots == 0) {
+      if (r > 0) break;
+    } else if (!persistent_task(prm, r, pq, ph)) {
+      break;
     }
-    __syncthreads();
-    if (G == 1) __syncthreads();  // group B runs one half-step behind
+    const Task tk = make_task<P, kRows, GEN>(prm, wave, pq, ph);
+    if (tk.empty) continue;  // the whole workgroup
+    const int N = tk.N;
+    const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(prm.k + tk.kv_slice * D, (uint32_t)N * D * 2);
+    const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(prm.v + tk.kv_slice * D, (uint32_t)N * D * 2);
 
-    // the loads of the matrix phase of step m, load i at k-step i
-    auto loads = [&](int m) {
-      return [&, m](int i) {
-        if (i < dt::kWaveLoads) {
-          if constexpr (G == 0) {
-            if (m == 1) dma.issue_one(rs, region(3), row_of(3), w4, i);
-            if (m >= 1) dma.issue_one(rs, region(m + 3), row_of(m + 3), w4, i);
-          } else {
-            dma.issue_one(rs, region(m + 2), row_of(m + 2), w4, i);
+    bf16x8 qf[g::kKSteps];
+    load_q<D>(prm, tk, l32, hh, qf);
+    const int k_lane = k_lane_off<D>(lane);
+    const int v_lane = v_lane_off<D>(lane);
+
+    f32x16 oacc[g::kDB];
+  #pragma unroll
+    for (int i = 0; i < g::kDB; ++i) oacc[i] = f32x16{};
+    RowState st;
+    const float c = prm.c;
+  #pragma unroll
+    for (int kk = 0; kk < g::kKSteps; ++kk) asm volatile("" : "+v"(qf[kk]) : : "memory");
+
+    const int count = tk.wg.count();
+    auto row_of = [&](int k) { return k < count ? tk.wg.tile(k) * kBN : N; };
+    auto ktile = [&](int j) { return (lchar *)smem + (j % kKSlots) * dt::kRegionB; };
+    auto vtile = [&](int j) {
+      return (lchar *)smem + (kKSlots + (j & (kVSlots - 1))) * dt::kRegionB;
+    };
+    auto sees = [&](int m) { return m < count && tk.w.has(tk.wg.tile(m)); };
+
+    // S of two tiles in flight: S(m) in sb[m % 2] is turned into weights while
+    // the MFMAs of S(m + 1) run.
+    f32x16 sb[2][2];
+    bf16x8 pf[2][2];
+    bf16x8 ka[3][2];
+    bf16x8 va[4];
+
+    // Group A stages K, group B stages V.
+    auto group_program = [&](auto grp_c) {
+      constexpr int G = decltype(grp_c)::value;
+      const int w4 = wave & 3;
+      // Step m >= 1 reads K(m + 1) (half-steps 2m, group A, and 2m + 1, group
+      // B), step 0 reads K(0) and K(1); V(j) is read in half-steps 2j + 2 and
+      // 2j + 3.  A slot's next tile is loaded (straight into LDS) once both
+      // groups have read the previous one: group A loads K(m + 3) in its
+      // matrix phase of step m >= 1 (K(3) too in step 1) and waits for K(m + 2)
+      // at the end of its softmax phase; group B loads V(m + 2) in its matrix
+      // phase of step m and waits for V(m) at its end.  The loads are spread
+      // over the phase's k-steps.  Loads past the last tile read outside the
+      // buffer (zero, no memory access), so the number of loads in flight does
+      // not depend on the tile count.
+      const __amdgpu_buffer_rsrc_t rs = G == 0 ? rs_k : rs_v;
+      dt dma;
+      dma.init(G == 0 ? g::kCh + 1 : g::kCh + 4, w4, lane);
+      auto region = [&](int j) { return (uint32_t)(uintptr_t)(G == 0 ? ktile(j) : vtile(j)); };
+      if constexpr (G == 0) {
+        dma.issue(rs, region(0), row_of(0), w4);
+        dma.issue(rs, region(1), row_of(1), w4);
+        dma.issue(rs, region(2), row_of(2), w4);
+        wait_loads<dt::kWaveLoads>();
+      } else {
+        dma.issue(rs, region(0), row_of(0), w4);
+        dma.issue(rs, region(1), row_of(1), w4);
+      }
+      __syncthreads();
+      if (G == 1) __syncthreads();  // group B runs one half-step behind
+
+      // the loads of the matrix phase of step m, load i at k-step i
+      auto loads = [&](int m) {
+        return [&, m](int i) {
+          if (i < dt::kWaveLoads) {
+            if constexpr (G == 0) {
+              if (m == 1) dma.issue_one(rs, region(3), row_of(3), w4, i);
+              if (m >= 1) dma.issue_one(rs, region(m + 3), row_of(m + 3), w4, i);
+            } else {
+              dma.issue_one(rs, region(m + 2), row_of(m + 2), w4, i);
+            }
+          }
+        };
+      };
+      auto no_loads = [](int) {};
+      auto prefetch_k = [&](int j) {  // K fragments of k-steps 0, 1 of tile j
+        const lchar *kb = ktile(j) + k_lane;
+        ka[0][0] = kfrag<D>(kb, 0, 0);
+        ka[0][1] = kfrag<D>(kb, 0, 1);
+        ka[1][0] = kfrag<D>(kb, 1, 0);
+        ka[1][1] = kfrag<D>(kb, 1, 1);
+      };
+      auto prefetch_v = [&](int j) {  // the first four V^T fragments of tile j
+        const lchar *vb = vtile(j) + v_lane;
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) va[i] = vfrag<D>(vb, i >> 2, (i >> 1) & 1, i & 1);
+      };
+      // Softmax phase of step m: weights P(m) from S(m) (zero if no row of
+      // the wave sees tile m).
+      auto vector = [&](int m, f32x16 (&s)[2]) {
+        if (sees(m)) {
+          mask_tile<GEN>(s, prm, tk.wg.tile(m) * kBN, tk.qw0, l32, hh, N);
+          softmax_pp<g::kDB>(s, pf, st, oacc, c);
+        } else {
+  #pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+  #pragma unroll
+            for (int tt = 0; tt < 2; ++tt) pf[rb][tt] = bf16x8{};
           }
         }
       };
-    };
-    auto no_loads = [](int) {};
-    auto prefetch_k = [&](int j) {  // K fragments of k-steps 0, 1 of tile j
-      const lchar *kb = ktile(j) + k_lane;
-      ka[0][0] = kfrag<D>(kb, 0, 0);
-      ka[0][1] = kfrag<D>(kb, 0, 1);
-      ka[1][0] = kfrag<D>(kb, 1, 0);
-      ka[1][1] = kfrag<D>(kb, 1, 1);
-    };
-    auto prefetch_v = [&](int j) {  // the first four V^T fragments of tile j
-      const lchar *vb = vtile(j) + v_lane;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) va[i] = vfrag<D>(vb, i >> 2, (i >> 1) & 1, i & 1);
-    };
-    // Softmax phase of step m: weights P(m) from S(m) (zero if no row of
-    // the wave sees tile m).
-    auto vector = [&](int m, f32x16 (&s)[2]) {
-      if (sees(m)) {
-        mask_tile<GEN>(s, prm, tk.wg.tile(m) * kBN, tk.qw0, l32, hh, N);
-        softmax_pp<g::kDB>(s, pf, st, oacc, c);
-      } else {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) pf[rb][tt] = bf16x8{};
-        }
-      }
-    };
-    // Matrix phase of step m: S(m + 1) and O += P(m - 1) V(m - 1).  Every
-    // wave runs the same MFMAs whatever its rows see (S of a tile past the
-    // last is computed from whatever the slot holds and never used): one
-    // code path keeps O in the same registers throughout.
-    auto matrix = [&](int m, f32x16 (&s_next)[2]) {
+      // Matrix phase of step m: S(m + 1) and O += P(m - 1) V(m - 1).  Every
+      // wave runs the same MFMAs whatever its rows see (S of a tile past the
+      // last is computed from whatever the slot holds and never used): one
+      // code path keeps O in the same registers throughout.
+      auto matrix = [&](int m, f32x16 (&s_next)[2]) {
+        __builtin_amdgcn_s_setprio(2);
+        prefetch_k(m + 1);
+        prefetch_v(m - 1);
+        mfma_phase<D, true, true>(ktile(m + 1) + k_lane, vtile(m - 1) + v_lane, qf, s_next, pf,
+                                  oacc, ka, va, st.lrnd, loads(m));
+        __builtin_amdgcn_s_setprio(0);
+        if constexpr (G == 1) wait_loads<2 * dt::kWaveLoads>();
+        __syncthreads();
+      };
+
+      // step 0: S(0) and S(1)
       __builtin_amdgcn_s_setprio(2);
-      prefetch_k(m + 1);
-      prefetch_v(m - 1);
-      mfma_phase<D, true, true>(ktile(m + 1) + k_lane, vtile(m - 1) + v_lane, qf, s_next, pf,
-                                oacc, ka, va, st.lrnd, loads(m));
+      prefetch_k(0);
+      mfma_phase<D, true, false>(ktile(0) + k_lane, nullptr, qf, sb[0], pf, oacc, ka, va,
+                                 st.lrnd, loads(0));
+      prefetch_k(1);
+      mfma_phase<D, true, false>(ktile(1) + k_lane, nullptr, qf, sb[1], pf, oacc, ka, va,
+                                 st.lrnd, no_loads);
       __builtin_amdgcn_s_setprio(0);
       if constexpr (G == 1) wait_loads<2 * dt::kWaveLoads>();
       __syncthreads();
-    };
-
-    // step 0: S(0) and S(1)
-    __builtin_amdgcn_s_setprio(2);
-    prefetch_k(0);
-    mfma_phase<D, true, false>(ktile(0) + k_lane, nullptr, qf, sb[0], pf, oacc, ka, va,
-                               st.lrnd, loads(0));
-    prefetch_k(1);
-    mfma_phase<D, true, false>(ktile(1) + k_lane, nullptr, qf, sb[1], pf, oacc, ka, va,
-                               st.lrnd, no_loads);
-    __builtin_amdgcn_s_setprio(0);
-    if constexpr (G == 1) wait_loads<2 * dt::kWaveLoads>();
-    __syncthreads();
-    vector(0, sb[0]);
-    if constexpr (G == 0) wait_loads<0>();
-    __syncthreads();
-    int m = 1;
-    for (;;) {
-      if (m == count) break;
-      matrix(m, sb[0]);  // S(m + 1), m odd
-      vector(m, sb[1]);
-      if constexpr (G == 0) {
-        // K(m + 2): after step 1, whose loads of K(3) and K(4) interleave,
-        // wait for all of them
-        if (m == 1) {
-          wait_loads<0>();
-        } else {
-          wait_loads<dt::kWaveLoads>();
+      vector(0, sb[0]);
+      if constexpr (G == 0) wait_loads<0>();
+      __syncthreads();
+      int m = 1;
+      for (;;) {
+        if (m == count) break;
+        matrix(m, sb[0]);  // S(m + 1), m odd
+        vector(m, sb[1]);
+        if constexpr (G == 0) {
+          // K(m + 2): after step 1, whose loads of K(3) and K(4) interleave,
+          // wait for all of them
+          if (m == 1) {
+            wait_loads<0>();
+          } else {
+            wait_loads<dt::kWaveLoads>();
+          }
         }
+        __syncthreads();
+        ++m;
+        if (m == count) break;
+        matrix(m, sb[1]);  // S(m + 1), m even
+        vector(m, sb[0]);
+        if constexpr (G == 0) wait_loads<dt::kWaveLoads>();
+        __syncthreads();
+        ++m;
       }
+      // last step: O += P(count - 1) V(count - 1)
+      __builtin_amdgcn_s_setprio(2);
+      prefetch_v(count - 1);
+      mfma_phase<D, false, true>(nullptr, vtile(count - 1) + v_lane, qf, sb[0], pf, oacc, ka, va,
+                                 st.lrnd, no_loads);
+      __builtin_amdgcn_s_setprio(0);
       __syncthreads();
-      ++m;
-      if (m == count) break;
-      matrix(m, sb[1]);  // S(m + 1), m even
-      vector(m, sb[0]);
-      if constexpr (G == 0) wait_loads<dt::kWaveLoads>();
-      __syncthreads();
-      ++m;
+      if (G == 0) __syncthreads();
+    };
+    if (grp == 0) {
+      group_program(std::integral_constant<int, 0>{});
+    } else {
+      group_program(std::integral_constant<int, 1>{});
     }
-    // last step: O += P(count - 1) V(count - 1)
-    __builtin_amdgcn_s_setprio(2);
-    prefetch_v(count - 1);
-    mfma_phase<D, false, true>(nullptr, vtile(count - 1) + v_lane, qf, sb[0], pf, oacc, ka, va,
-                               st.lrnd, no_loads);
-    __builtin_amdgcn_s_setprio(0);
-    __syncthreads();
-    if (G == 0) __syncthreads();
-  };
-  if (grp == 0) {
-    group_program(std::integral_constant<int, 0>{});
-  } else {
-    group_program(std::integral_constant<int, 1>{});
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load left in flight
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load left in flight
 
-  write_out<D>(prm, tk, l32, hh, oacc, st);
+    write_out<D>(prm, tk, l32, hh, oacc, st);
+    // every wave has passed the tile's last barrier, after its last LDS read:
+    // the next tile's loads may overwrite the rings
+  }
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 template <int D, int P>
-hipError_t launch_pp_t(const FwdProblem &p, hipStream_t stream) {
+hipError_t launch_pp_t(const FwdProblem &p, hipStream_t stream, bool persistent) {
   constexpr int kRows = 32 * 8 / P;
   Params prm{};
   prm.q = static_cast<const uint16_t *>(p.q);
@@ -1117,18 +1181,26 @@ hipError_t launch_pp_t(const FwdProblem &p, hipStream_t stream) {
   prm.neg = p.scale < 0.0f ? 1 : 0;
   prm.causal = p.causal;
   prm.window = p.window;
+  // persistent: one workgroup per CU, when every XCD has a head group and
+  // every slot at least two tiles
+  const int slots = device_cus() / 8;
+  unsigned grid = prm.total;
+  if (persistent && slots > 0 && p.B * prm.groups >= 8 && prm.total >= 16 * slots) {
+    prm.slots = slots;
+    grid = 8 * slots;
+  }
   void *args[] = {&prm};
   return hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_pp_kernel<D, P, false>),
-                         dim3(prm.total), dim3(512), args, 0, stream);
+                         dim3(grid), dim3(512), args, 0, stream);
 }
 
 template <int D>
-hipError_t launch_pp(const FwdProblem &p, hipStream_t stream) {
+hipError_t launch_pp(const FwdProblem &p, hipStream_t stream, bool persistent) {
   const int G = p.Hq / p.Hkv;
-  if (G % 8 == 0) return launch_pp_t<D, 8>(p, stream);
-  if (G % 4 == 0) return launch_pp_t<D, 4>(p, stream);
-  if (G % 2 == 0) return launch_pp_t<D, 2>(p, stream);
-  return launch_pp_t<D, 1>(p, stream);
+  if (G % 8 == 0) return launch_pp_t<D, 8>(p, stream, persistent);
+  if (G % 4 == 0) return launch_pp_t<D, 4>(p, stream, persistent);
+  if (G % 2 == 0) return launch_pp_t<D, 2>(p, stream, persistent);
+  return launch_pp_t<D, 1>(p, stream, persistent);
 }
 
 template <int D, int NW, int P>
@@ -1261,7 +1333,7 @@ hipError_t launch_nw(const FwdProblem &p, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_d(const FwdProblem &p, int v, hipStream_t stream) {
-  if (v == kPingPong) return launch_pp<D>(p, stream);
+  if (v == kPingPong || v == kPersistent) return launch_pp<D>(p, stream, v == kPersistent);
   return v == kWaves4 ? launch_nw<D, 4>(p, stream) : launch_nw<D, 8>(p, stream);
 }
 
@@ -1273,14 +1345,16 @@ const char *variant_name(int variant) {
     case kWaves4: return "w4_bn64_mfma32x32x16";
     case kWaves8: return "w8_bn64_mfma32x32x16";
     case kPingPong: return "w8_pingpong_bn64_mfma32x32x16";
+    case kPersistent: return "w8_pingpong_persistent_bn64_mfma32x32x16";
   }
   return "invalid";
 }
 
 hipError_t launch_fwd(const FwdProblem &p, int variant, hipStream_t stream) {
-  // default: 8 waves at d = 128 (one workgroup per CU); 4 waves at d = 64,
-  // where 138 VGPRs let three 4-wave workgroups share a CU
-  const int v = variant != kAuto ? variant : p.d == 64 ? kWaves4 : kPingPong;
+  // default: at d = 128 the ping-pong kernel, persistent (one workgroup per
+  // CU) when the problem has enough tiles; at d = 64 the 4-wave lockstep
+  // kernel, where 138 VGPRs let three 4-wave workgroups share a CU
+  const int v = variant != kAuto ? variant : p.d == 64 ? kWaves4 : kPersistent;
   return p.d == 128 ? launch_d<128>(p, v, stream) : launch_d<64>(p, v, stream);
 }
 

@@ -25,7 +25,8 @@ enum Variant : int {
   kWaves4 = 1,  // 4 waves (256 threads) per workgroup, 32 query rows per wave
   kWaves8 = 2,  // 8 waves (512 threads) per workgroup, 32 query rows per wave
   kPingPong = 3,  // 8 waves in two groups that alternate matrix and softmax phases
-  kNumVariants = 4
+  kPersistent = 4,  // the same kernel, one workgroup per CU running several tiles
+  kNumVariants = 5
 };
 
 const char *variant_name(int variant);

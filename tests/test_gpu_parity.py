@@ -86,7 +86,7 @@ SHAPES = [
 ]
 
 
-VARIANTS = [1, 2, 3]  # every explicit kernel variant
+VARIANTS = [1, 2, 3, 4]  # every explicit kernel variant
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -99,6 +99,43 @@ def test_parity_small_shapes(shape, variant):
     o_ref, l_ref = attention_forward(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(d), causal,
                                      window)
     check(o, lse, o_ref, l_ref, f"{shape} v{variant}")
+
+
+# shapes with enough tiles for the persistent schedule (one workgroup per CU,
+# head groups split over the XCDs, tiles dealt in alternating rounds),
+# including head-group counts that do not divide by 8 and ragged N
+PERSISTENT_SHAPES = [
+    (2, 32, 32, 2048, 128, True, 0),
+    (1, 64, 8, 4096, 128, True, 0),     # 8 heads per workgroup
+    (1, 32, 32, 8192, 128, True, 1000),
+    (2, 16, 16, 4096, 128, False, 0),
+    (1, 12, 12, 16000, 128, True, 0),   # 12 head groups over 8 XCDs
+    (2, 24, 6, 5000, 128, True, 300),   # 4 heads per workgroup, 12 head groups
+    (3, 10, 10, 4400, 64, True, 0),
+]
+
+
+@pytest.mark.parametrize("shape", PERSISTENT_SHAPES, ids=[str(s) for s in PERSISTENT_SHAPES])
+def test_persistent_schedule_is_bitwise_the_ping_pong_kernel(shape):
+    """Variant 4 runs the tiles of variant 3 in another order on fewer
+    workgroups; every tile's arithmetic is the same, so O and lse agree
+    bitwise, and every tile is written (guard values would show)."""
+    B, Hq, Hkv, N, d, causal, window = shape
+    say(f"case persistent {shape}")
+    q, k, v = make_qkv(B, Hq, Hkv, N, d, seed=77 + N)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    res = []
+    for var in (3, 4):
+        o = torch.full((B, Hq, N, d), 7.0, dtype=torch.bfloat16, device=DEV)
+        lse = torch.full((B, Hq, N), 7.0, dtype=torch.float32, device=DEV)
+        attn.fwd(qd, kd, vd, causal=causal, window=window, variant=var, out=(o, lse))
+        torch.cuda.synchronize()
+        res.append((o.cpu(), lse.cpu()))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+    if shape == PERSISTENT_SHAPES[0]:
+        o_ref, l_ref = attention_forward(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(d),
+                                         causal, window, workers=16)
+        check(res[1][0], res[1][1], o_ref, l_ref, str(shape))
 
 
 def test_variants_agree():
