@@ -59,8 +59,9 @@ def kernel_sha(kind: str = "fwd") -> str:
     """sha256[:16] of one kind of kernel's code (KERNEL_SOURCES; the forward's
     is KERNEL_SRC): its source and the device header it includes, with //
     comments, trailing blanks and empty lines removed, and the device compile
-    flags.  A comment edit keeps stored counter data valid; any change to the
-    code or the flags invalidates it."""
+    flags other than include paths (which name the directory the repository
+    sits in).  A comment edit or a move of the repository keeps stored counter
+    data valid; any change to the code or the flags invalidates it."""
     from exact_tiled_attention_attn_amd.build import DEVICE_ONLY, COMMON
     src = KERNEL_SRC if kind == "fwd" else os.path.join(CSRC, KERNEL_SOURCES[kind])
     code = []
@@ -70,7 +71,7 @@ def kernel_sha(kind: str = "fwd") -> str:
                 line = line.split("//", 1)[0].rstrip()
                 if line:
                     code.append(line)
-    code.append(" ".join(COMMON + DEVICE_ONLY))
+    code.append(" ".join(f for f in COMMON + DEVICE_ONLY if not f.startswith("-I")))
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 

@@ -100,3 +100,12 @@ def test_peaks_from_device_properties():
     import pytest
     with pytest.raises(RuntimeError):
         bench.derive_peaks((0, 2400000, 0, 0), 0, 0)
+
+
+def test_kernel_sha_does_not_depend_on_where_the_repository_sits(monkeypatch):
+    from exact_tiled_attention_attn_amd import build
+    h1 = bench.kernel_sha()
+    moved = [f.replace(build.ROOT, "/elsewhere/repo") for f in build.COMMON]
+    assert moved != build.COMMON
+    monkeypatch.setattr(build, "COMMON", moved)
+    assert bench.kernel_sha() == h1
