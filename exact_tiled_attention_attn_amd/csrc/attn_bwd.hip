@@ -201,8 +201,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(BwdParams prm) 
     const lchar *kt = set + kKb + kt_lane;
     const lchar *vb = set + kKb + kKt + kb_lane;
     const int j0 = t * kBN;
-    const bool need_mask = (prm.causal && j0 + kBN - 1 > tk.qw0) ||
-                           (prm.window > 0 && j0 <= tk.qw0 + 31 - prm.window) || (j0 + kBN > N);
+    const bool need_mask = edge_tile(prm.causal, prm.window, j0, kBN, tk.qw0, N);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       // the next tile's LDS stores go out between the two key blocks, when

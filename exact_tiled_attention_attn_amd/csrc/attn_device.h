@@ -111,9 +111,58 @@ __device__ __forceinline__ bf16x8 tr_frag(const lchar *base, int db, int rb, int
   return __builtin_bit_cast(bf16x8, both);
 }
 
-// Which (batch, query head, rows, key tiles) a wave of a query-tiled
-// workgroup owns: kRows query rows per workgroup, P heads per workgroup
-// (wave w serves head w % P on rows (w / P) * 32 ..), key tiles of KBN keys.
+// Launch order of the query-tiled kernels (the forwards and the backward's
+// dQ kernel): a workgroup serves query-tile rank qrank of head group
+// hgb = batch * groups + head group, P heads per workgroup (wave w serves
+// head w % P on rows (w / P) * 32 ..); causal ranks run heaviest first
+// (rank 0 is the last row tile).  Prm must provide groups, nq, causal, G.
+struct TileSlot {
+  int b, head, kvh;
+  int wg_r0;  // first query row of the workgroup
+  int qw0;    // first query row of this wave
+};
+
+template <int P, int kRows, class Prm>
+__device__ __forceinline__ TileSlot tile_slot(const Prm &prm, int wave, int qrank, int hgb) {
+  TileSlot t;
+  const int hg = hgb % prm.groups;
+  t.b = hgb / prm.groups;
+  const int qi = prm.causal ? (prm.nq - 1 - qrank) : qrank;  // heaviest tiles first
+  t.head = hg * P + (wave % P);
+  t.kvh = __builtin_amdgcn_readfirstlane((hg * P) / prm.G);  // P divides G
+  t.wg_r0 = qi * kRows;
+  t.qw0 = t.wg_r0 + (wave / P) * 32;
+  return t;
+}
+
+// One workgroup per query tile: hardware workgroup id -> (qrank, hgb), the
+// logical id xcd_remap(id) = hgb * nq + qrank, so the tiles of one head run
+// behind one L2.  Prm must provide total and nq.
+template <class Prm>
+__device__ __forceinline__ void dense_slot(const Prm &prm, int id, int &qrank, int &hgb) {
+  const int logical = xcd_remap(id, prm.total);
+  qrank = logical % prm.nq;
+  hgb = logical / prm.nq;
+}
+
+// Keys [lo, hi) that query rows [r0, r1) of an N-row sequence may see under
+// the causal mask and the causal window (row i sees i - window < j <= i).
+__device__ __forceinline__ void causal_window_keys(int causal, int window, int r0, int r1, int N,
+                                                   int &lo, int &hi) {
+  hi = causal ? r1 : N;
+  lo = window > 0 ? max(0, r0 - window + 1) : 0;
+}
+
+// Whether the 32 query rows from qw0 hold a pair of keys [j0, j0 + kbn)
+// that is masked (diagonal, window edge) or past N: only such tiles run
+// the mask.
+__device__ __forceinline__ bool edge_tile(int causal, int window, int j0, int kbn, int qw0,
+                                          int N) {
+  return (causal && j0 + kbn - 1 > qw0) || (window > 0 && j0 <= qw0 + 31 - window) ||
+         (j0 + kbn > N);
+}
+
+// The dense task of a query-tiled workgroup with KBN-key tiles.
 // Prm must provide total, nq, groups, causal, window, G, nkt, N, Hq, Hkv.
 struct Task {
   int b, head, kvh;
@@ -126,23 +175,22 @@ struct Task {
 
 template <int P, int kRows, int KBN, class Prm>
 __device__ __forceinline__ Task make_task(const Prm &prm, int wave) {
+  int qrank, hgb;
+  dense_slot(prm, blockIdx.x, qrank, hgb);
+  const TileSlot sl = tile_slot<P, kRows>(prm, wave, qrank, hgb);
   Task tk;
-  const int logical = xcd_remap(blockIdx.x, prm.total);
-  const int qrank = logical % prm.nq;
-  const int hgb = logical / prm.nq;
-  const int hg = hgb % prm.groups;
-  tk.b = hgb / prm.groups;
-  const int qi = prm.causal ? (prm.nq - 1 - qrank) : qrank;  // heaviest tiles first
-  tk.head = hg * P + (wave % P);
-  tk.kvh = __builtin_amdgcn_readfirstlane((hg * P) / prm.G);  // P divides G
-  const int wg_r0 = qi * kRows;
-  tk.qw0 = wg_r0 + (wave / P) * 32;
+  tk.b = sl.b;
+  tk.head = sl.head;
+  tk.kvh = sl.kvh;
+  tk.qw0 = sl.qw0;
   const int N = prm.N;
   auto tile_range = [&](int r0, int r1, int &lo, int &hi) {  // rows [r0, r1)
-    hi = prm.causal ? min(prm.nkt, (r1 - 1) / KBN + 1) : prm.nkt;
-    lo = prm.window > 0 ? max(0, r0 - prm.window + 1) / KBN : 0;
+    int klo, khi;
+    causal_window_keys(prm.causal, prm.window, r0, r1, N, klo, khi);
+    lo = klo / KBN;
+    hi = min(prm.nkt, (khi + KBN - 1) / KBN);
   };
-  tile_range(wg_r0, min(N, wg_r0 + kRows), tk.wg_lo, tk.wg_hi);
+  tile_range(sl.wg_r0, min(N, sl.wg_r0 + kRows), tk.wg_lo, tk.wg_hi);
   if (tk.qw0 < N) {
     tile_range(tk.qw0, min(N, tk.qw0 + 32), tk.w_lo, tk.w_hi);
   } else {

@@ -321,8 +321,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void attn_fwd_fp8_kernel(
       }
     }
     // mask: register r of block rb holds key j0 + 32 rb + 8 (r / 4) + 4 hh + r % 4
-    const bool need_mask = (prm.causal && j0 + kBN8 - 1 > tk.qw0) ||
-                           (prm.window > 0 && j0 <= tk.qw0 + 31 - prm.window) || (j0 + kBN8 > N);
+    const bool need_mask = edge_tile(prm.causal, prm.window, j0, kBN8, tk.qw0, N);
     if (need_mask) {
       const int kb0 = j0 + 4 * hh;
       const unsigned span = (unsigned)max(m_hi - m_lo, 0);

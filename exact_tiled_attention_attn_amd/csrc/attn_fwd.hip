@@ -78,7 +78,11 @@ using dev::make_rsrc;
 using dev::u32x4;
 using dev::wave_max_pair;
 using dev::wave_sum_pair;
-using dev::xcd_remap;
+using dev::causal_window_keys;
+using dev::dense_slot;
+using dev::edge_tile;
+using dev::tile_slot;
+using dev::TileSlot;
 
 constexpr int kBN = 64;              // keys per tile
 constexpr float kTau = 8.0f;         // lazy-rescale threshold, log2 units
@@ -179,7 +183,9 @@ struct Segs {
 
 // Rows [r0, r1) of a sequence of N rows (r0 < r1 <= N).
 __device__ __forceinline__ Segs key_segments(const Params &prm, int r0, int r1, int N) {
-  const int hi_c = prm.causal ? r1 : N;  // keys past this are never seen
+  int lo, hi;
+  causal_window_keys(prm.causal, prm.window, r0, r1, N, lo, hi);
+  const int hi_c = hi;  // keys past this are never seen
   Segs sg;
   if (r0 < prm.nglob) {  // a global row sees every key it may
     sg.a_hi = 0;
@@ -187,8 +193,6 @@ __device__ __forceinline__ Segs key_segments(const Params &prm, int r0, int r1, 
     sg.b_hi = (hi_c + kBN - 1) / kBN;
     return sg;
   }
-  int lo = 0, hi = hi_c;
-  if (prm.window > 0) lo = max(lo, r0 - prm.window + 1);
   if (prm.radius > 0) {
     lo = max(lo, r0 - prm.radius);
     hi = min(hi, r1 + prm.radius);
@@ -305,17 +309,14 @@ __device__ __forceinline__ Task make_task(const Params &prm, int wave, int pq = 
       hgb = blockIdx.x % nbh;
     }
   } else {
-    const int logical = xcd_remap(blockIdx.x, prm.total);
-    qrank = logical % prm.nq;
-    hgb = logical / prm.nq;
+    dense_slot(prm, blockIdx.x, qrank, hgb);
   }
-  const int hg = hgb % prm.groups;
-  tk.b = hgb / prm.groups;
-  const int qi = prm.causal ? (prm.nq - 1 - qrank) : qrank;  // heaviest tiles first
-  tk.head = hg * P + (wave % P);
-  tk.kvh = __builtin_amdgcn_readfirstlane((hg * P) / prm.G);  // P divides G
-  const int wg_r0 = qi * kRows;
-  tk.qw0 = wg_r0 + (wave / P) * 32;
+  const TileSlot sl = tile_slot<P, kRows>(prm, wave, qrank, hgb);
+  tk.b = sl.b;
+  tk.head = sl.head;
+  tk.kvh = sl.kvh;
+  tk.qw0 = sl.qw0;
+  const int wg_r0 = sl.wg_r0;
   int N;
   if constexpr (GEN) {
     // offsets clamped into [0, total_rows]: an inconsistent table yields
@@ -400,8 +401,7 @@ struct RowState {
 // rows qw0.. cannot see: the causal diagonal, the window edge and the tile
 // holding key N - 1.  Wave-uniform.
 __device__ __forceinline__ bool tile_needs_mask(const Params &prm, int j0, int qw0, int N) {
-  return (prm.causal && j0 + kBN - 1 > qw0) ||
-         (prm.window > 0 && j0 <= qw0 + 31 - prm.window) || (j0 + kBN > N);
+  return edge_tile(prm.causal, prm.window, j0, kBN, qw0, N);
 }
 
 // Scores of keys this lane's row cannot see become -inf (no branches).
@@ -415,16 +415,27 @@ __device__ __forceinline__ void apply_mask(f32x16 (&s)[2], const Params &prm, in
   const int kbase = j0 + 4 * hh;
   int hi = N - 1 - kbase;
   if (prm.causal) hi = min(hi, qrow - kbase);
-  const int lo = prm.window > 0 ? qrow - prm.window - kbase : -1 - kbase;
-  const unsigned span = (unsigned)max(hi - lo, 0);
-  const int lo1 = lo + 1;
+  if (prm.window > 0 && j0 <= qw0 + 31 - prm.window) {  // the window's lower edge too
+    const int lo = qrow - prm.window - kbase;
+    const unsigned span = (unsigned)max(hi - lo, 0);
+    const int lo1 = lo + 1;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int off = 32 * rb + 8 * (r >> 2) + (r & 3);
-      const bool vis = (unsigned)(off - lo1) < span;
-      s[rb][r] = vis ? s[rb][r] : -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        const int off = 32 * rb + 8 * (r >> 2) + (r & 3);
+        const bool vis = (unsigned)(off - lo1) < span;
+        s[rb][r] = vis ? s[rb][r] : -INFINITY;
+      }
+    }
+  } else {  // only an upper edge (the diagonal, N): one signed compare per score
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 32 * rb + 8 * (r >> 2) + (r & 3);
+        s[rb][r] = off <= hi ? s[rb][r] : -INFINITY;
+      }
     }
   }
 }
@@ -957,7 +968,6 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(Params prm) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;  // 0: group A (stages K), 1: group B (stages V)
-  const int gt = tid & 255;
   const int l32 = lane & 31, hh = lane >> 5;
 
   for (int r = 0;; ++r) {
