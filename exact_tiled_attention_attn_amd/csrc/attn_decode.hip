@@ -299,23 +299,35 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(DecParams prm) {
   }
 }
 
-// Merges the splits of one (sequence, KV head, column): one wave; the
-// lanes first reduce the splits' lse maximum, then each lane accumulates
-// D / 64 values of O over the splits.  Only splits of a sequence that holds
-// keys matter; the others have lse = -inf.
-template <int D>
-__global__ __launch_bounds__(64) void attn_decode_merge_kernel(DecParams prm) {
+// Merges the splits of one (sequence, KV head, column): W waves, wave w
+// taking the splits w, w + W, ...; the threads first reduce the splits' lse
+// maximum, then each lane of a wave accumulates D / 64 values of O over its
+// wave's splits, and wave 0 adds the W partial sums.  Only splits of a
+// sequence that holds keys matter; the others have lse = -inf.  W = 4 when
+// there are many splits (the walk over them is the merge's latency), else 1.
+template <int D, int kMergeWaves>
+__global__ __launch_bounds__(64 * kMergeWaves) void attn_decode_merge_kernel(DecParams prm) {
   constexpr int kPer = D / 64;  // d values per lane
-  const int lane = threadIdx.x;
+  __shared__ float red[kMergeWaves];
+  __shared__ float part_acc[kMergeWaves][64 * kPer];
+  __shared__ float part_tot[kMergeWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int col = blockIdx.x % prm.ncols;
   const int bk = blockIdx.x / prm.ncols;
   const int b = bk / prm.Hkv, kvh = bk % prm.Hkv;
   const size_t slot0 = (size_t)bk * prm.nsplit * prm.ncols + col;
   float m = -INFINITY;
-  for (int s = lane; s < prm.nsplit; s += 64)
+  for (int s = tid; s < prm.nsplit; s += 64 * kMergeWaves)
     m = fmaxf(m, prm.part_lse[slot0 + (size_t)s * prm.ncols]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if constexpr (kMergeWaves > 1) {
+    if (lane == 0) red[wv] = m;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) m = fmaxf(m, red[w]);
+  }
   // every split wrote its slot (an empty one o = 0, lse = -inf, whose weight
   // exp(-inf - m) is 0), so the walk is branch-free; eight splits per step
   // keep eight loads in flight per lane
@@ -323,12 +335,13 @@ __global__ __launch_bounds__(64) void attn_decode_merge_kernel(DecParams prm) {
   float tot = 0.0f;
   if (m > -INFINITY) {
     constexpr int kU = 8;
-    for (int s0 = 0; s0 < prm.nsplit; s0 += kU) {
+    for (int s0 = wv; s0 < prm.nsplit; s0 += kU * kMergeWaves) {
       float ls[kU], ov[kU][kPer];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const bool in = s0 + u < prm.nsplit;
-        const size_t slot = slot0 + (size_t)(in ? s0 + u : 0) * prm.ncols;
+        const int sp = s0 + u * kMergeWaves;
+        const bool in = sp < prm.nsplit;
+        const size_t slot = slot0 + (size_t)(in ? sp : 0) * prm.ncols;
         ls[u] = in ? prm.part_lse[slot] : -INFINITY;
         const float *po = prm.part_o + slot * D + lane * kPer;
 #pragma unroll
@@ -341,6 +354,19 @@ __global__ __launch_bounds__(64) void attn_decode_merge_kernel(DecParams prm) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) acc[j] += w * ov[u][j];
       }
+    }
+  }
+  if constexpr (kMergeWaves > 1) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) part_acc[wv][lane * kPer + j] = acc[j];
+    if (lane == 0) part_tot[wv] = tot;
+    __syncthreads();
+    if (wv != 0) return;
+#pragma unroll
+    for (int w = 1; w < kMergeWaves; ++w) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) acc[j] += part_acc[w][lane * kPer + j];
+      tot += part_tot[w];
     }
   }
   const int g = col / prm.T, t = col % prm.T;
@@ -401,7 +427,10 @@ hipError_t launch_decode_d(const DecodeProblem &p, const DecodePlan &plan, hipSt
   if (e != hipSuccess) return e;
   const long long merges = groups * prm.ncols;
   if (merges > 0x7fffffffLL) return hipErrorInvalidValue;
-  return hipLaunchKernel(reinterpret_cast<const void *>(&attn_decode_merge_kernel<D>),
+  if (plan.nsplit >= 64)
+    return hipLaunchKernel(reinterpret_cast<const void *>(&attn_decode_merge_kernel<D, 4>),
+                           dim3((unsigned)merges), dim3(256), args, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void *>(&attn_decode_merge_kernel<D, 1>),
                          dim3((unsigned)merges), dim3(64), args, 0, stream);
 }
 
