@@ -111,6 +111,11 @@ struct Params {
   int nglob;
   int compact;    // sequence lengths differ: launch only non-empty tiles first
   int slots;      // persistent launch: workgroups per XCD (0: one per tile)
+  // global rows computed by workgroups of their own (global_rows_task): the
+  // first ngtask workgroups of the launch; the others treat global rows as
+  // local ones and do not write them
+  int gsplit;
+  int ngtask;
 };
 
 template <int D>
@@ -187,7 +192,7 @@ __device__ __forceinline__ Segs key_segments(const Params &prm, int r0, int r1, 
   causal_window_keys(prm.causal, prm.window, r0, r1, N, lo, hi);
   const int hi_c = hi;  // keys past this are never seen
   Segs sg;
-  if (r0 < prm.nglob) {  // a global row sees every key it may
+  if (r0 < prm.nglob && !prm.gsplit) {  // a global row sees every key it may
     sg.a_hi = 0;
     sg.b_lo = 0;
     sg.b_hi = (hi_c + kBN - 1) / kBN;
@@ -298,15 +303,16 @@ __device__ __forceinline__ Task make_task(const Params &prm, int wave, int pq = 
     // (dealt round-robin to the XCDs) spread every sequence over all XCDs
     if (prm.compact) {
       int b, hg;
-      if (!compact_slot<kRows>(prm, blockIdx.x, qrank, b, hg)) {
+      if (!compact_slot<kRows>(prm, (int)blockIdx.x - prm.ngtask, qrank, b, hg)) {
         tk.empty = true;
         return tk;
       }
       hgb = b * prm.groups + hg;
     } else {
       const int nbh = prm.B * prm.groups;
-      qrank = blockIdx.x / nbh;
-      hgb = blockIdx.x % nbh;
+      const int id = (int)blockIdx.x - prm.ngtask;
+      qrank = id / nbh;
+      hgb = id % nbh;
     }
   } else {
     dense_slot(prm, blockIdx.x, qrank, hgb);
@@ -404,7 +410,11 @@ __device__ __forceinline__ bool tile_needs_mask(const Params &prm, int j0, int q
   return edge_tile(prm.causal, prm.window, j0, kBN, qw0, N);
 }
 
-// Scores of keys this lane's row cannot see become -inf (no branches).
+// Scores of keys this lane's row cannot see become -inf.  SPLIT (the
+// ping-pong kernel): tiles with no window edge take one signed compare per
+// score, the others the range compare; the lockstep kernels keep the single
+// range compare (a second code path there cost registers and spills).
+template <bool SPLIT>
 __device__ __forceinline__ void apply_mask(f32x16 (&s)[2], const Params &prm, int j0, int qw0,
                                            int l32, int hh, int N) {
   // Register r of block rb holds key kbase + off with the compile-time
@@ -415,8 +425,8 @@ __device__ __forceinline__ void apply_mask(f32x16 (&s)[2], const Params &prm, in
   const int kbase = j0 + 4 * hh;
   int hi = N - 1 - kbase;
   if (prm.causal) hi = min(hi, qrow - kbase);
-  if (prm.window > 0 && j0 <= qw0 + 31 - prm.window) {  // the window's lower edge too
-    const int lo = qrow - prm.window - kbase;
+  if (!SPLIT || (prm.window > 0 && j0 <= qw0 + 31 - prm.window)) {  // a lower edge too
+    const int lo = prm.window > 0 ? qrow - prm.window - kbase : -1 - kbase;
     const unsigned span = (unsigned)max(hi - lo, 0);
     const int lo1 = lo + 1;
 #pragma unroll
@@ -445,7 +455,7 @@ __device__ __forceinline__ void apply_mask(f32x16 (&s)[2], const Params &prm, in
 //    ((window <= 0 or j > i - window) and (radius <= 0 or |i - j| <= radius))).
 __device__ __forceinline__ bool tile_needs_mask_gen(const Params &prm, int j0, int qw0, int N) {
   if (j0 + kBN > N || (prm.causal && j0 + kBN - 1 > qw0)) return true;
-  if (qw0 + 31 < prm.nglob || j0 + kBN - 1 < prm.nglob) return false;
+  if ((qw0 + 31 < prm.nglob && !prm.gsplit) || j0 + kBN - 1 < prm.nglob) return false;
   const bool win_ok = prm.window <= 0 || j0 > qw0 + 31 - prm.window;
   const bool rad_ok = prm.radius <= 0 ||
                       (j0 >= qw0 + 31 - prm.radius && j0 + kBN - 1 <= qw0 + prm.radius);
@@ -455,12 +465,16 @@ __device__ __forceinline__ bool tile_needs_mask_gen(const Params &prm, int j0, i
 // The keys row i sees are two ranges: the global keys [0, gcap) and the
 // local range [lo, hi] (for a global row: every key it may see).  With the
 // per-register offset off (key = kbase + off), each is one unsigned compare.
+// SPLIT (the ping-pong kernel): a tile with no global key takes the local
+// range compare alone (the lockstep kernels' register budget has no room for
+// the second code path).
+template <bool SPLIT>
 __device__ __forceinline__ void apply_mask_gen(f32x16 (&s)[2], const Params &prm, int j0,
                                                int qw0, int l32, int hh, int N) {
   const int i = qw0 + l32;
   const int hi_c = prm.causal ? min(i, N - 1) : N - 1;  // last key causality allows
   int lo = 0, hi = hi_c;
-  if (i >= prm.nglob) {
+  if (i >= prm.nglob || prm.gsplit) {
     if (prm.window > 0) lo = max(lo, i - prm.window + 1);
     if (prm.radius > 0) {
       lo = max(lo, i - prm.radius);
@@ -471,6 +485,17 @@ __device__ __forceinline__ void apply_mask_gen(f32x16 (&s)[2], const Params &prm
   const int kbase = j0 + 4 * hh;
   const int a = kbase - lo;                       // key - lo = off + a
   const unsigned span = (unsigned)max(hi - lo + 1, 0);
+  if (SPLIT && j0 >= prm.nglob) {  // no global key in the tile: the local range alone
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 32 * rb + 8 * (r >> 2) + (r & 3);
+        s[rb][r] = (unsigned)(off + a) < span ? s[rb][r] : -INFINITY;
+      }
+    }
+    return;
+  }
   const unsigned gspan = (unsigned)max(gcap, 0);  // key < gcap
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
@@ -483,13 +508,13 @@ __device__ __forceinline__ void apply_mask_gen(f32x16 (&s)[2], const Params &prm
   }
 }
 
-template <bool GEN>
+template <bool GEN, bool SPLIT = false>
 __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], const Params &prm, int j0, int qw0,
                                           int l32, int hh, int N) {
   if constexpr (GEN) {
-    if (tile_needs_mask_gen(prm, j0, qw0, N)) apply_mask_gen(s, prm, j0, qw0, l32, hh, N);
+    if (tile_needs_mask_gen(prm, j0, qw0, N)) apply_mask_gen<SPLIT>(s, prm, j0, qw0, l32, hh, N);
   } else {
-    if (tile_needs_mask(prm, j0, qw0, N)) apply_mask(s, prm, j0, qw0, l32, hh, N);
+    if (tile_needs_mask(prm, j0, qw0, N)) apply_mask<SPLIT>(s, prm, j0, qw0, l32, hh, N);
   }
 }
 
@@ -500,15 +525,22 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], const Params &prm, int
 // P = exp2(c*S - m2) packed to bf16 as the B operand of the PV MFMAs; both
 // running sums.  Returns whether m2 moved; the caller then multiplies O by
 // `alpha` before the next PV MFMA.
+// NB: key blocks of 32 in the tile (2; 1 for the 32-key tiles of the global
+// rows, whose second block is unused).
+template <int NB = 2>
 __device__ __forceinline__ bool softmax_core(const f32x16 (&s)[2], bf16x8 (&pf)[2][2],
                                              RowState &st, float c, float &alpha) {
-  float mq[4];  // four independent max chains
+  float mq[4];  // independent max chains, two per block
 #pragma unroll
-  for (int j = 0; j < 4; ++j) mq[j] = fmaxf(s[j >> 1][8 * (j & 1)], s[j >> 1][8 * (j & 1) + 1]);
+  for (int j = 0; j < 2 * NB; ++j) mq[j] = fmaxf(s[j >> 1][8 * (j & 1)], s[j >> 1][8 * (j & 1) + 1]);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2 * NB; ++j) {
 #pragma unroll
     for (int e = 2; e < 8; ++e) mq[j] = fmaxf(mq[j], s[j >> 1][8 * (j & 1) + e]);
+  }
+  if constexpr (NB == 1) {
+    mq[2] = mq[0];
+    mq[3] = mq[1];
   }
   const float mx = wave_max_pair(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
   const float mt2 = mx * c;
@@ -521,7 +553,7 @@ __device__ __forceinline__ bool softmax_core(const f32x16 (&s)[2], bf16x8 (&pf)[
   const float negm = -st.m2;
   float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent add chains
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < NB; ++rb) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
@@ -540,7 +572,7 @@ __device__ __forceinline__ bool softmax_core(const f32x16 (&s)[2], bf16x8 (&pf)[
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float rp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < NB; ++rb) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
@@ -554,24 +586,26 @@ __device__ __forceinline__ bool softmax_core(const f32x16 (&s)[2], bf16x8 (&pf)[
   return move;
 }
 
-template <int KDB>
+template <int KDB, int NB = 2>
 __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], bf16x8 (&pf)[2][2],
                                              RowState &st, f32x16 (&oacc)[KDB], float c) {
   float alpha;
-  if (softmax_core(s, pf, st, c, alpha)) {
+  if (softmax_core<NB>(s, pf, st, c, alpha)) {
 #pragma unroll
     for (int i = 0; i < KDB; ++i) oacc[i] *= alpha;
   }
 }
 
-// Epilogue: O = O / lrnd (bf16, RNE) and lse = ln(lsum) + max.
+// Epilogue: O = O / lrnd (bf16, RNE) and lse = ln(lsum) + max, for rows
+// row_lo .. N - 1 (rows below row_lo belong to global_rows_task).
 template <int D>
 __device__ __forceinline__ void write_out(const Params &prm, const Task &tk, int l32, int hh,
-                                          const f32x16 (&oacc)[Geo<D>::kDB], const RowState &st) {
+                                          const f32x16 (&oacc)[Geo<D>::kDB], const RowState &st,
+                                          int row_lo = 0) {
   const float ltot = wave_sum_pair(st.lsum);
   const float lrtot = wave_sum_pair(st.lrnd);
   const int row = tk.qw0 + l32;
-  if (row >= tk.N) return;
+  if (row >= tk.N || row < row_lo) return;
   const float inv = 1.0f / lrtot;
   uint16_t *op = prm.o + tk.q_slice * D + (size_t)row * D + 4 * hh;
 #pragma unroll
@@ -585,6 +619,173 @@ __device__ __forceinline__ void write_out(const Params &prm, const Task &tk, int
     }
   }
   if (hh == 0) prm.lse[tk.q_slice + row] = (st.m2 + __builtin_amdgcn_logf(ltot)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// Global rows (Longformer's global tokens, general mode).  A global row sees
+// every key, so the workgroup holding one would run the whole key range
+// while the others run their band: it would set the end of the launch.
+// Instead the first ngtask workgroups of the launch each take one block of
+// 32 global rows of one (sequence, query head) and split its keys over four
+// waves: wave w runs the 32-key tiles w, w + 4, ... on its own LDS quarter
+// (one wave's LDS instructions run in order, so no barrier is needed
+// between a tile's reads and the next tile's stores), with the forward's
+// arithmetic (lazy reference max, P in bf16, both sums).  The four partial
+// states (m, l, l~, O) are then merged through LDS by the rule the running
+// softmax uses: M = max_w m_w, each part weighted by 2^(m_w - M).  The
+// other workgroups treat the global rows as local ones and do not write
+// them.
+// ---------------------------------------------------------------------------
+template <int D>
+struct HalfTile {  // 32 keys of K and V in registers: 16-byte chunks per lane
+  using g = Geo<D>;
+  static constexpr int kN = 32 * g::kCh / 64;  // chunks per lane per tensor
+  u32x4 k[kN], v[kN];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                       int j0, int lane) {
+#pragma unroll
+    for (int n = 0; n < kN; ++n) {
+      const int ci = n * 64 + lane, r = ci / g::kCh, c = ci % g::kCh;
+      const uint32_t off = (uint32_t)(j0 + r) * g::kRowB + c * 16;
+      k[n] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+      v[n] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(lchar *kt, lchar *vt, int lane) const {
+#pragma unroll
+    for (int n = 0; n < kN; ++n) {
+      const int ci = n * 64 + lane, r = ci / g::kCh, c = ci % g::kCh;
+      *(lds_u32x4_t *)(kt + r * g::kKStride + c * 16) = k[n];
+      *(lds_u32x4_t *)(vt + r * g::kVStride + c * 16) = v[n];
+    }
+  }
+};
+
+template <int D>
+__device__ __forceinline__ void global_rows_task(const Params &prm, char *smem) {
+  using g = Geo<D>;
+  constexpr int kW = 4;                          // waves that split the keys
+  constexpr int kQuarterB = g::kSetB / 2;        // 32-key K tile + 32-key V tile
+  constexpr int kVOff = 32 * g::kKStride;
+  static_assert(kW * kQuarterB <= 2 * g::kSetB, "four quarters in the two buffer sets");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  const int ngb = (prm.nglob + 31) / 32;
+  const int gb = (int)blockIdx.x % ngb, bh = (int)blockIdx.x / ngb;
+  const int h = bh % prm.Hq, b = bh / prm.Hq;
+  const int start = min(max(prm.cu[b], 0), prm.total_rows);
+  const int N = max(min(prm.cu[b + 1], prm.total_rows) - start, 0);
+  const int nrows = min(prm.nglob, N);  // global rows of this sequence
+  Task tk;
+  tk.b = b;
+  tk.head = h;
+  tk.kvh = h / prm.G;
+  tk.N = N;
+  tk.qw0 = 32 * gb;
+  tk.q_slice = (size_t)h * prm.total_rows + start;
+  tk.kv_slice = (size_t)tk.kvh * prm.total_rows + start;
+  if (tk.qw0 >= nrows) return;  // the whole workgroup
+
+  f32x16 oacc[g::kDB];
+#pragma unroll
+  for (int i = 0; i < g::kDB; ++i) oacc[i] = f32x16{};
+  RowState st;
+  const float c = prm.c;
+  if (wave < kW) {
+    bf16x8 qf[g::kKSteps];
+    load_q<D>(prm, tk, l32, hh, qf);
+#pragma unroll
+    for (int kk = 0; kk < g::kKSteps; ++kk) asm volatile("" : "+v"(qf[kk]) : : "memory");
+    lchar *const kt = (lchar *)smem + wave * kQuarterB;
+    lchar *const vt = kt + kVOff;
+    const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(prm.k + tk.kv_slice * D, (uint32_t)N * D * 2);
+    const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(prm.v + tk.kv_slice * D, (uint32_t)N * D * 2);
+    const int row = tk.qw0 + l32;
+    const int kend = prm.causal ? min(N, tk.qw0 + 32) : N;  // keys any row of the block sees
+    const int nt = (kend + 31) / 32;
+    const lchar *kb = kt + k_lane_off<D>(lane);
+    const lchar *vb = vt + v_lane_off<D>(lane);
+    // S^T of 32-key tile j from the wave's LDS quarter, mask, softmax, PV
+    auto compute = [&](int j) {
+      f32x16 sc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int kk = 0; kk < g::kKSteps; ++kk)
+        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag<D>(kb, kk, 0), qf[kk], sc[0], 0, 0, 0);
+      // register r holds key 32 j + 8 (r / 4) + 4 hh + r % 4; a global row
+      // sees every key below N (and, causal, up to itself)
+      const int j0 = 32 * j;
+      if (j0 + 31 >= N || (prm.causal && j0 + 31 > tk.qw0)) {
+        const int hi = (prm.causal ? min(row, N - 1) : N - 1) - (j0 + 4 * hh);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sc[0][r] = 8 * (r >> 2) + (r & 3) <= hi ? sc[0][r] : -INFINITY;
+      }
+      bf16x8 pf[2][2];
+      softmax_tile<g::kDB, 1>(sc, pf, st, oacc, c);  // one block of 32 keys
+#pragma unroll
+      for (int db = 0; db < g::kDB; ++db) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag<D>(vb, db, 0, tt), pf[0][tt],
+                                                             oacc[db], 0, 0, 0);
+      }
+    };
+    // tiles j = wave, wave + 4, ...: staged through registers, the next
+    // one loading while this one is computed (a second stage would not fit
+    // the d = 64 kernel's register budget of three workgroups per CU)
+    HalfTile<D> sa;
+    if (wave < nt) sa.load(rs_k, rs_v, 32 * wave, lane);
+    for (int j = wave; j < nt; j += kW) {
+      sa.store(kt, vt, lane);
+      if (j + kW < nt) sa.load(rs_k, rs_v, 32 * (j + kW), lane);
+      compute(j);
+    }
+  }
+  __syncthreads();  // every wave's tile reads are done: the LDS takes the partial states
+  // per wave: m, l, l~ (64 lanes each), then O^T in accumulator order
+  constexpr int kStateF = 3 * 64 + g::kDB * 16 * 64;
+  static_assert(kW * kStateF * 4 <= 2 * g::kSetB, "partial states fit the LDS");
+  float *const part = (float *)smem;
+  if (wave < kW) {
+    float *const mine = part + wave * kStateF;
+    mine[lane] = st.m2;
+    mine[64 + lane] = st.lsum;
+    mine[128 + lane] = st.lrnd;
+#pragma unroll
+    for (int db = 0; db < g::kDB; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mine[192 + (db * 16 + r) * 64 + lane] = oacc[db][r];
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float mx = part[lane];
+#pragma unroll
+  for (int w = 1; w < kW; ++w) mx = fmaxf(mx, part[w * kStateF + lane]);
+  RowState tot;
+  tot.m2 = mx;
+  tot.lsum = 0.0f;
+  tot.lrnd = 0.0f;
+#pragma unroll
+  for (int db = 0; db < g::kDB; ++db) oacc[db] = f32x16{};
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    const float *const pw = part + w * kStateF;
+    const float e = __builtin_amdgcn_exp2f(pw[lane] - mx);  // 0 for a part with no key
+    tot.lsum += e * pw[64 + lane];
+    tot.lrnd += e * pw[128 + lane];
+#pragma unroll
+    for (int db = 0; db < g::kDB; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] += e * pw[192 + (db * 16 + r) * 64 + lane];
+    }
+  }
+  Task out = tk;
+  out.N = nrows;  // write the global rows only
+  write_out<D>(prm, out, l32, hh, oacc, tot);
 }
 
 // ---------------------------------------------------------------------------
@@ -606,6 +807,12 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D == 64) ? 3 : 2) void attn_fw
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
 
+  if constexpr (GEN) {
+    if ((int)blockIdx.x < prm.ngtask) {
+      global_rows_task<D>(prm, smem);
+      return;
+    }
+  }
   const Task tk = make_task<P, kRows, GEN>(prm, wave);
   if (tk.empty) return;  // the whole workgroup: its tile lies past its sequence
   const int N = tk.N;
@@ -719,7 +926,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D == 64) ? 3 : 2) void attn_fw
   if (k < count) step(k, set0, set1, stage1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load left in flight
 
-  write_out<D>(prm, tk, l32, hh, oacc, st);
+  write_out<D>(prm, tk, l32, hh, oacc, st, prm.gsplit ? prm.nglob : 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -970,7 +1177,10 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(Params prm) {
   const int grp = wave >> 2;  // 0: group A (stages K), 1: group B (stages V)
   const int l32 = lane & 31, hh = lane >> 5;
 
-  for (int r = 0;; ++r) {
+  // One query tile per pass: the workgroup's own in the one-workgroup-per-
+  // tile launch (a single pass, straight-line code in the general mode), or
+  // the persistent schedule's next.
+  for (int r = 0; GEN ? r < 1 : true; ++r) {
     int pq = -1, ph = -1;
     if (GEN || prm.slots == 0) {
       if (r > 0) break;
@@ -1071,7 +1281,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(Params prm) {
       // the wave sees tile m).
       auto vector = [&](int m, f32x16 (&s)[2]) {
         if (sees(m)) {
-          mask_tile<GEN>(s, prm, tk.wg.tile(m) * kBN, tk.qw0, l32, hh, N);
+          mask_tile<GEN, true>(s, prm, tk.wg.tile(m) * kBN, tk.qw0, l32, hh, N);
           softmax_pp<g::kDB>(s, pf, st, oacc, c);
         } else {
   #pragma unroll
@@ -1275,9 +1485,16 @@ hipError_t launch_gen_t(const VarlenProblem &p, hipStream_t stream) {
   prm.radius = p.radius;
   prm.nglob = p.n_global;
   prm.compact = (long long)p.B * p.max_seqlen != p.total_rows;
+  // global rows: workgroups of their own, placed first in the launch
+  if (p.n_global > 0) {
+    const long long ngt = (long long)p.B * p.Hq * ((p.n_global + 31) / 32);
+    if (ngt + prm.total > 0x7fffffffLL) return hipErrorInvalidValue;
+    prm.gsplit = 1;
+    prm.ngtask = (int)ngt;
+  }
   void *args[] = {&prm};
   return hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_kernel<D, NW, P, true>),
-                         dim3(prm.total), dim3(NW * 64), args, 0, stream);
+                         dim3(prm.total + prm.ngtask), dim3(NW * 64), args, 0, stream);
 }
 
 template <int D, int P>
@@ -1315,11 +1532,13 @@ hipError_t launch_gen_pp_t(const VarlenProblem &p, hipStream_t stream) {
 template <int D>
 hipError_t launch_gen_d(const VarlenProblem &p, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
-  if constexpr (D == 128) {  // the ping-pong kernel, as the dense default
-    if (G % 8 == 0) return launch_gen_pp_t<D, 8>(p, stream);
-    if (G % 4 == 0) return launch_gen_pp_t<D, 4>(p, stream);
-    if (G % 2 == 0) return launch_gen_pp_t<D, 2>(p, stream);
-    return launch_gen_pp_t<D, 1>(p, stream);
+  if constexpr (D == 128) {  // the ping-pong kernel, as the dense default, without global rows
+    if (p.n_global == 0) {
+      if (G % 8 == 0) return launch_gen_pp_t<D, 8>(p, stream);
+      if (G % 4 == 0) return launch_gen_pp_t<D, 4>(p, stream);
+      if (G % 2 == 0) return launch_gen_pp_t<D, 2>(p, stream);
+      return launch_gen_pp_t<D, 1>(p, stream);
+    }
   }
   if constexpr (kGenWaves<D> >= 8) {
     if (G % 8 == 0) return launch_gen_t<D, 8>(p, stream);

@@ -68,6 +68,8 @@ CASES = [
     ([777, 33], 8, 2, 128, False, 0, 0, 64),            # globals, no band: full rows
     ([2048, 5, 1500], 16, 2, 128, False, 0, 256, 16),   # Longformer-like
     ([4096], 4, 4, 64, False, 0, 256, 300),             # more globals than a tile
+    ([31, 32, 33, 100, 1], 4, 4, 64, True, 0, 8, 33),   # two global blocks, short sequences
+    ([3000, 40], 8, 4, 128, False, 0, 128, 20),         # d = 128 Longformer-like
     # more than 64 sequences of different lengths: the compacted launch
     # order scans the lengths in chunks of 64 per wave
     ([int(x) for x in np.random.default_rng(7).integers(0, 300, size=150)],
