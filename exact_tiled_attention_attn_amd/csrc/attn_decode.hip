@@ -299,6 +299,201 @@ __global__ __launch_bounds__(64) void attn_decode_split_kernel(DecParams prm) {
   }
 }
 
+// More than 32 columns per KV head (multi-query attention at real head
+// counts, several new tokens): one workgroup of W waves per (sequence,
+// split, KV head, group of W column blocks), wave w computing column block
+// W g + w.  The waves share each K/V tile: every wave gathers 1 / W of its
+// rows, the tile goes to one of two LDS sets, and a barrier per tile
+// publishes it; the compute is the single-wave kernel's.
+template <int D, int kPol, int W>
+struct DecStageW {
+  using tl = DecTile<D>;
+  static constexpr int kM = tl::kLoads / W;  // loads per lane per tensor
+  static_assert(kM * W == tl::kLoads, "W must divide the loads of a tile");
+  u32x4 k[kM], v[kM];
+  // load n = W m + wave of the single-wave kernel's order (rows
+  // n * kRowsPerLoad + lane / kCh, 16-byte chunk lane % kCh)
+  __device__ __forceinline__ void load(const DecParams &prm, int page0, int page1, int j0, int L,
+                                       int kvh, int lane, int wave) {
+    const __amdgpu_buffer_rsrc_t k0 = group_rsrc<D>(prm.kc, prm, page0, j0, L, kvh);
+    const __amdgpu_buffer_rsrc_t k1 = group_rsrc<D>(prm.kc, prm, page1, j0 + 16, L, kvh);
+    const __amdgpu_buffer_rsrc_t v0 = group_rsrc<D>(prm.vc, prm, page0, j0, L, kvh);
+    const __amdgpu_buffer_rsrc_t v1 = group_rsrc<D>(prm.vc, prm, page1, j0 + 16, L, kvh);
+    const uint32_t stride = (uint32_t)prm.Hkv * D * 2;
+    const int r_lane = lane / Stride<D>::kCh, ch = lane % Stride<D>::kCh;
+#pragma unroll
+    for (int m = 0; m < kM; ++m) {
+      const int n = W * m + wave;
+      const int r = n * tl::kRowsPerLoad + r_lane;  // tile row 0 .. 31
+      const uint32_t off = (uint32_t)(r & 15) * stride + ch * 16;
+      const bool hi = n * tl::kRowsPerLoad >= 16;   // wave-uniform
+      k[m] = __builtin_amdgcn_raw_buffer_load_b128(hi ? k1 : k0, off, 0, kPol);
+      v[m] = __builtin_amdgcn_raw_buffer_load_b128(hi ? v1 : v0, off, 0, kPol);
+    }
+  }
+  __device__ __forceinline__ void store(lchar *set, int lane, int wave) const {
+    const int r_lane = lane / Stride<D>::kCh, ch = lane % Stride<D>::kCh;
+#pragma unroll
+    for (int m = 0; m < kM; ++m) {
+      const int r = (W * m + wave) * tl::kRowsPerLoad + r_lane;
+      *(lds_u32x4_t *)(set + r * Stride<D>::kB128 + ch * 16) = k[m];
+      *(lds_u32x4_t *)(set + tl::kKB + r * Stride<D>::kTr + ch * 16) = v[m];
+    }
+  }
+};
+
+template <int D, int kPol, int W>
+__global__ __launch_bounds__(64 * W) void attn_decode_split_mc_kernel(DecParams prm) {
+  using st = Stride<D>;
+  using tl = DecTile<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * tl::kSet];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  // item w and group gi of its ceil(ncb / W) column-block groups: with more
+  // than one group, group gi of item w is workgroup 8 (ngr (w / 8) + gi) + w % 8
+  // (same XCD as the item's other groups, 8 ids apart)
+  const int ngr = (prm.ncb + W - 1) / W;
+  const int u = blockIdx.x;
+  const int gi = ngr == 1 ? 0 : (u >> 3) % ngr;
+  const int w = ngr == 1 ? u : ((u >> 3) / ngr) * 8 + (u & 7);
+  if (w >= prm.nwork) return;  // padding of the last group of 8 items
+  const int kvh = w % prm.Hkv;
+  const int bs = w / prm.Hkv;
+  const int split = bs % prm.nsplit, b = bs / prm.nsplit;
+  const int bk = b * prm.Hkv + kvh;
+  const int L = prm.lens[b];
+  const int T = prm.T;
+
+  const int col = 32 * (W * gi + wave) + l32;
+  const bool col_ok = col < prm.ncols;
+  const int g = col_ok ? col / T : 0, t = col_ok ? col % T : 0;
+  const int pos = L - T + t;
+  const int m_lo = prm.window > 0 ? max(0, pos - prm.window + 1) : 0;
+  const int m_span = col_ok && pos >= 0 ? pos - m_lo + 1 : 0;
+
+  const int lo_all = prm.window > 0 ? max(0, L - T - prm.window + 1) : 0;
+  const int s_lo = (lo_all / prm.unit) * prm.unit + split * prm.chunk;
+  const int k_begin = max(s_lo, lo_all & ~(kKeys - 1));
+  const int k_end = min(s_lo + prm.chunk, L);
+  const int ntiles = k_end > k_begin ? (k_end - k_begin + kKeys - 1) / kKeys : 0;
+
+  const int e0 = s_lo >> prm.ps_shift;
+  int entry = -1;
+  if (e0 + lane < prm.max_pages && lane < kMaxEntries)
+    entry = prm.table[(size_t)b * prm.max_pages + e0 + lane];
+  auto page_of = [&](int j) { return __builtin_amdgcn_readlane(entry, (j >> prm.ps_shift) - e0); };
+
+  const size_t q_row = ((size_t)(b * prm.Hq + kvh * prm.G + g) * T + t);
+  bf16x8 qf[st::kKSteps];
+#pragma unroll
+  for (int kk = 0; kk < st::kKSteps; ++kk) {
+    qf[kk] = row_frag<D>(prm.q + q_row * D, 0, col_ok ? 1 : 0, 16 * kk + 8 * hh, prm.neg);
+    settle(qf[kk]);
+  }
+  settle(entry);
+
+  f32x16 oacc[st::kDB];
+#pragma unroll
+  for (int i = 0; i < st::kDB; ++i) oacc[i] = f32x16{};
+  float m2 = -1e30f, lsum = 0.0f, lrnd = 0.0f;
+  const float c = prm.c;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const int kb_lane = b128_lane_off<st::kB128>(lane);
+  const int vt_lane = tr_lane_off<st::kTr>(lane);
+
+  auto compute = [&](int j0, const lchar *set) {
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < st::kKSteps; ++kk)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b128_frag<st::kB128>(set + kb_lane, kk, 0),
+                                                  qf[kk], s, 0, 0, 0);
+    const bool need_mask = (prm.window > 0 && j0 < L - prm.window) || j0 + kKeys - 1 > L - T;
+    if (need_mask) {
+      const int base = j0 + 4 * hh - m_lo;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        s[r] = (unsigned)(base + 8 * (r >> 2) + (r & 3)) < (unsigned)m_span ? s[r] : -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = wave_max_pair(mx) * c;
+    const float mnew = fmaxf(m2, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+    m2 = mnew;
+    bf16x8 pf[2];
+    float ps = 0.0f, pr = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -mnew));
+      ps += p;
+      pf[r >> 3][r & 7] = (__bf16)p;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bf16x2 pair = {pf[i >> 2][2 * (i & 3)], pf[i >> 2][2 * (i & 3) + 1]};
+      pr = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, pr, false);
+    }
+    lsum = lsum * alpha + wave_sum_pair(ps);
+    lrnd = lrnd * alpha + wave_sum_pair(pr);
+#pragma unroll
+    for (int db = 0; db < st::kDB; ++db) {
+      oacc[db] *= alpha;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tr_frag<st::kTr>(set + tl::kKB + vt_lane, db, 0, tt), pf[tt], oacc[db], 0, 0, 0);
+    }
+  };
+
+  // Tile i sits in LDS set i % 2; while it is computed, tile i + 1 (loaded
+  // a step earlier) goes to the other set and tile i + 2 starts loading.
+  // One barrier per tile: a set is rewritten only after every wave has
+  // passed the barrier that ends its computation.
+  auto set_of = [&](int i) { return (lchar *)smem + (i & 1) * tl::kSet; };
+  auto tile_j0 = [&](int i) { return k_begin + i * kKeys; };
+  DecStageW<D, kPol, W> stage;
+  auto issue = [&](int i) {
+    const int j0 = tile_j0(i);
+    stage.load(prm, page_of(j0), page_of(j0 + 16), j0, L, kvh, lane, wave);
+  };
+  if (ntiles > 0) {
+    issue(0);
+    stage.store(set_of(0), lane, wave);
+    if (ntiles > 1) issue(1);
+  }
+  __syncthreads();
+  for (int i = 0; i < ntiles; ++i) {
+    compute(tile_j0(i), set_of(i));
+    if (i + 1 < ntiles) {
+      stage.store(set_of(i + 1), lane, wave);
+      if (i + 2 < ntiles) issue(i + 2);
+    }
+    __syncthreads();
+  }
+
+  const bool any = lsum > 0.0f;
+  const float lse_s = any ? (m2 + __log2f(lsum)) * kLn2 : -INFINITY;
+  const float inv = any ? 1.0f / lrnd : 0.0f;
+  if (col_ok) {
+    const size_t slot = ((size_t)bk * prm.nsplit + split) * prm.ncols + col;
+    float *po = prm.part_o + slot * D + 4 * hh;
+#pragma unroll
+    for (int db = 0; db < st::kDB; ++db) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 wv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wv[j] = oacc[db][4 * i + j] * inv;
+        *(f32x4 *)(po + 32 * db + 8 * i) = wv;
+      }
+    }
+    if (hh == 0) prm.part_lse[slot] = lse_s;
+  }
+}
+
 // Merges the splits of one (sequence, KV head, column): W waves, wave w
 // taking the splits w, w + W, ...; the threads first reduce the splits' lse
 // maximum, then each lane of a wave accumulates D / 64 values of O over its
@@ -408,7 +603,11 @@ hipError_t launch_decode_d(const DecodeProblem &p, const DecodePlan &plan, hipSt
   prm.window = p.window;
   const long long groups = (long long)p.B * p.Hkv;
   const long long items = groups * plan.nsplit;
-  const long long wgs = prm.ncb == 1 ? items : (items + 7) / 8 * 8 * prm.ncb;
+  // more than one column block: W waves per workgroup, one per block, and
+  // ceil(ncb / W) workgroups per item
+  const int W = prm.ncb >= 4 ? 4 : prm.ncb >= 2 ? 2 : 1;
+  const int ngr = (prm.ncb + W - 1) / W;
+  const long long wgs = ngr == 1 ? items : (items + 7) / 8 * 8 * ngr;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
   prm.nwork = (int)items;
   void *args[] = {&prm};
@@ -416,14 +615,22 @@ hipError_t launch_decode_d(const DecodeProblem &p, const DecodePlan &plan, hipSt
   // the 256 MB last-level cache can stay there from one call to the next
   // and is read with ordinary loads; a larger one is streamed with
   // nontemporal loads (measured: 7-10 % faster at 1.9 GB, 9 % slower at
-  // 135 MB, where ordinary loads hit the last-level cache).
-  // Column blocks after the first read their K/V tiles from L2, which a
+  // 135 MB, where ordinary loads hit the last-level cache).  Workgroups of
+  // one item after the first read its K/V tiles from L2, which a
   // nontemporal load would not have kept: those calls use ordinary loads.
   const double kv_bytes = (double)groups * plan.nsplit * plan.chunk * D * 4.0;
-  const void *split = kv_bytes > kLastLevelCacheBytes && prm.ncb == 1
-                          ? reinterpret_cast<const void *>(&attn_decode_split_kernel<D, 2>)
-                          : reinterpret_cast<const void *>(&attn_decode_split_kernel<D, 0>);
-  hipError_t e = hipLaunchKernel(split, dim3((unsigned)wgs), dim3(64), args, 0, stream);
+  const bool nt = kv_bytes > kLastLevelCacheBytes && ngr == 1;
+  const void *split;
+  if (W == 4)
+    split = nt ? reinterpret_cast<const void *>(&attn_decode_split_mc_kernel<D, 2, 4>)
+               : reinterpret_cast<const void *>(&attn_decode_split_mc_kernel<D, 0, 4>);
+  else if (W == 2)
+    split = nt ? reinterpret_cast<const void *>(&attn_decode_split_mc_kernel<D, 2, 2>)
+               : reinterpret_cast<const void *>(&attn_decode_split_mc_kernel<D, 0, 2>);
+  else
+    split = nt ? reinterpret_cast<const void *>(&attn_decode_split_kernel<D, 2>)
+               : reinterpret_cast<const void *>(&attn_decode_split_kernel<D, 0>);
+  hipError_t e = hipLaunchKernel(split, dim3((unsigned)wgs), dim3(64 * W), args, 0, stream);
   if (e != hipSuccess) return e;
   const long long merges = groups * prm.ncols;
   if (merges > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -458,6 +665,11 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int T, int d, int page_size, int 
   const long long groups = (long long)B * Hkv;
   long long want = (4096 + groups * ncb - 1) / (groups * ncb);
   long long chunk = (span + want - 1) / want;
+  // with several column blocks a workgroup of several waves takes each
+  // split: at least 1024 keys (32 tiles) per split (measured: 64 heads on
+  // one KV head +17 % against 512 keys; 16 heads x 4 tokens, already at
+  // 1024, lose 16 % at 2048)
+  if (ncb > 1 && chunk < 1024) chunk = 1024;
   chunk = (chunk + unit - 1) / unit * unit;
   if (chunk < unit) chunk = unit;
   if (chunk > max_chunk) chunk = max_chunk;
