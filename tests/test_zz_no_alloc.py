@@ -63,6 +63,18 @@ def _both(p):
     return (o1.cpu(), l1.cpu()), (o2.cpu(), l2.cpu())
 
 
+def test_noalloc_matches_the_workspace_entry_point_with_many_columns():
+    """More than 32 query columns per KV head (the multi-wave kernel):
+    multi-query at 64 heads, then 16 heads x 4 tokens with a window."""
+    for label, p in (("multi-query 64/1", _problem(4, 64, 1, 1, 128, 64, 40000, seed=31)),
+                     ("16 heads x 4 tokens, window", _problem(2, 32, 2, 4, 64, 16, 9000, seed=32,
+                                                             window=2000))):
+        say(f"case noalloc {label}")
+        (o1, l1), (o2, l2) = _both(p)
+        assert torch.equal(o1, o2), label
+        assert torch.equal(l1, l2), label
+
+
 def test_noalloc_matches_the_workspace_entry_point_on_two_calls_in_a_row():
     big = _problem(8, 64, 8, 1, 128, 64, 131072, seed=21)
     small = _problem(3, 16, 2, 4, 128, 32, 3000, seed=7, window=700)
