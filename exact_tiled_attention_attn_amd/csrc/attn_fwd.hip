@@ -1086,8 +1086,10 @@ __device__ __forceinline__ void mfma_phase(const lchar *kb, const lchar *vb,
   using g = Geo<D>;
   static_assert(g::kPV == 2 * g::kKSteps, "two PV MFMAs per S k-step");
   // The sum of the bf16 weights as the PV MFMAs use them (O is normalized by
-  // it): one v_dot2 against (1, 1) per packed pair of weights, issued between
-  // the MFMAs (in the softmax phase these wait for the other wave's MFMAs).
+  // it): one v_dot2 against (1, 1) per packed pair of weights, in four
+  // partial sums.  The compiler issues them after the phase's last MFMA, in
+  // its shadow; in the softmax phase they waited for the other wave's MFMAs,
+  // and pinned between the MFMAs (one chain) the phase measured slower.
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float rp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   auto vf = [&](int i) { return vfrag<D>(vb, i >> 2, (i >> 1) & 1, i & 1); };
