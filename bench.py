@@ -55,6 +55,14 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def fwd_kernel_name(d: int, variant: int) -> str:
+    """The forward kernel a launch runs: variants 3 and 4 (and the default at
+    d = 128) are the ping-pong kernel, 1 and 2 (and the default at d = 64)
+    the lockstep one."""
+    v = variant if variant != 0 else (1 if d == 64 else 4)
+    return "attn_fwd_pp_kernel" if v in (3, 4) else "attn_fwd_kernel"
+
+
 def kernel_sha(kind: str = "fwd") -> str:
     """sha256[:16] of one kind of kernel's code (KERNEL_SOURCES; the forward's
     is KERNEL_SRC): its source and the device header it includes, with //
@@ -450,7 +458,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic_for(fwd_key(w.name, args.variant), sha),
-            "kernel": "attn_fwd_kernel",
+            "kernel": fwd_kernel_name(w.d, args.variant),
             "avg_launch_ms": round(ev_ms, 4),
             "flops_per_launch": f,
             "algorithmic_bytes_per_launch": algorithmic_bytes(w),

@@ -71,6 +71,20 @@ def test_forward_traffic_keys_name_the_variant():
     assert bench.fwd_key("c2", 2) == "c2@v2"
 
 
+def test_roofline_names_the_kernel_the_variant_runs():
+    """The line's roofline.kernel follows the library's dispatch: the
+    ping-pong variants (and the d = 128 default) run attn_fwd_pp_kernel,
+    whose trace is the committed forward profile."""
+    from exact_tiled_attention_attn_amd import attn
+    for v in (1, 2, 3, 4):
+        pp = "pingpong" in attn.attn_variant_name(v)
+        assert (bench.fwd_kernel_name(128, v) == "attn_fwd_pp_kernel") == pp, v
+    assert bench.fwd_kernel_name(128, 0) == "attn_fwd_pp_kernel"
+    assert bench.fwd_kernel_name(64, 0) == "attn_fwd_kernel"
+    assert os.path.exists(os.path.join(ROOT, "profiles",
+                                       "attn_fwd_pp_kernel_c2_c2sharp_c3_c4_c5_c5w.md"))
+
+
 def test_kernel_kinds_hash_their_own_source():
     shas = {k: bench.kernel_sha(k) for k in bench.KERNEL_SOURCES}
     assert shas["fwd"] == shas["varlen"] == bench.kernel_sha()
