@@ -944,8 +944,12 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D == 64) ? 3 : 2) void attn_fw
 // matrix pipe whatever the other wave queued behind it.
 //
 // Staging: group A loads the K tiles, group B the V tiles, HBM -> LDS
-// directly (no registers), into rings of three K and four V slots; the
-// loads of a matrix phase are spread over its k-steps.
+// directly (no registers), into rings of four K and four V slots (160 KiB
+// at d = 128); the loads of a matrix phase are spread over its k-steps.  A
+// tile is published one half-step before the matrix phase that first reads
+// it, so each wave reads that phase's first K and V^T fragments at the end
+// of its softmax phase, and they land while it waits at the barrier: the
+// phase opens with an MFMA instead of an LDS round trip.
 //
 // Launch: one workgroup per query tile, or persistent (persistent_task):
 // one workgroup per CU that runs its share of the tiles one after another,
@@ -965,6 +969,18 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
                :
                : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
                : "memory");
+}
+
+// Workgroup barrier that leaves this wave's LDS reads in flight: the next
+// matrix phase's first K and V^T fragments are read just before it and land
+// while the wave waits.  s_barrier alone (no release fence, which would wait
+// for them first); the memory clobber keeps the compiler from moving loads
+// across it.  No wave writes the LDS with ordinary stores in this kernel, so
+// the fence has nothing else to order.
+__device__ __forceinline__ void barrier_keep_reads() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Wait until at most N of this wave's vector memory loads are outstanding.
@@ -1073,8 +1089,8 @@ __device__ __forceinline__ void softmax_pp(f32x16 (&s)[2], bf16x8 (&pf)[2][2], R
 }
 
 // The matrix phase: S^T = K Q^T (DO_S) and O^T += V^T P^T (DO_PV),
-// interleaved two MFMAs of each per k-step; hook(j) runs at the start of
-// k-step j (the tile loads, spread over the phase).  On entry ka[0], ka[1]
+// interleaved two MFMAs of each per k-step; hook(j) runs after the S MFMAs
+// of k-step j (the tile loads, spread over the phase).  On entry ka[0], ka[1]
 // hold the K fragments of k-steps 0 and 1 and va[0..3] the first four V^T
 // fragments.
 template <int D, bool DO_S, bool DO_PV, class Hook>
@@ -1167,8 +1183,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(Params prm) {
   using g = Geo<D>;
   constexpr int kRows = 32 * 8 / P;  // query rows per workgroup
   using dt = DmaTile<D>;
-  constexpr int kKSlots = 3;  // K ring
-  constexpr int kVSlots = 4;  // V ring
+  constexpr int kKSlots = 4;  // K ring
+  constexpr int kVSlots = 4;  // V ring (8 slots: 160 KiB of LDS at d = 128)
   static_assert(g::kVTileB == dt::kRegionB, "a V tile fills its region");
 
   __shared__ __attribute__((aligned(1024))) char smem[(kKSlots + kVSlots) * dt::kRegionB];
@@ -1210,7 +1226,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(Params prm) {
 
     const int count = tk.wg.count();
     auto row_of = [&](int k) { return k < count ? tk.wg.tile(k) * kBN : N; };
-    auto ktile = [&](int j) { return (lchar *)smem + (j % kKSlots) * dt::kRegionB; };
+    auto ktile = [&](int j) { return (lchar *)smem + (j & (kKSlots - 1)) * dt::kRegionB; };
     auto vtile = [&](int j) {
       return (lchar *)smem + (kKSlots + (j & (kVSlots - 1))) * dt::kRegionB;
     };
@@ -1227,16 +1243,20 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(Params prm) {
     auto group_program = [&](auto grp_c) {
       constexpr int G = decltype(grp_c)::value;
       const int w4 = wave & 3;
-      // Step m >= 1 reads K(m + 1) (half-steps 2m, group A, and 2m + 1, group
-      // B), step 0 reads K(0) and K(1); V(j) is read in half-steps 2j + 2 and
-      // 2j + 3.  A slot's next tile is loaded (straight into LDS) once both
-      // groups have read the previous one: group A loads K(m + 3) in its
-      // matrix phase of step m >= 1 (K(3) too in step 1) and waits for K(m + 2)
-      // at the end of its softmax phase; group B loads V(m + 2) in its matrix
-      // phase of step m and waits for V(m) at its end.  The loads are spread
-      // over the phase's k-steps.  Loads past the last tile read outside the
-      // buffer (zero, no memory access), so the number of loads in flight does
-      // not depend on the tile count.
+      // Half-step h: group A runs matrix(m) at h = 2m and vector(m) at
+      // 2m + 1, group B one half-step later.  matrix(m) reads K(m + 1) and
+      // V(m - 1); its first fragments are read at the end of the softmax
+      // phase before it, so tile j must be published (loads landed, then a
+      // barrier) one half-step before that: K(j) by the end of half-step
+      // 2j - 4, V(j) by the end of 2j.  A slot's next tile is loaded
+      // (straight into LDS) once both groups have read the previous one.
+      // Group A loads K(m + 4) in its matrix phase of step m >= 1 (K(4) too in
+      // step 1; K(0..3) before step 0) and waits for K(m + 2) at the end of
+      // that phase; group B loads V(m + 2) in its matrix phase of step m and
+      // waits for V(m + 1) at the end of its softmax phase of step m.  The
+      // loads are spread over the phase's k-steps.  Loads past the last tile
+      // read outside the buffer (zero, no memory access), so the number of
+      // loads in flight does not depend on the tile count.
       const __amdgpu_buffer_rsrc_t rs = G == 0 ? rs_k : rs_v;
       dt dma;
       dma.init(G == 0 ? g::kCh + 1 : g::kCh + 4, w4, lane);
@@ -1245,21 +1265,24 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(Params prm) {
         dma.issue(rs, region(0), row_of(0), w4);
         dma.issue(rs, region(1), row_of(1), w4);
         dma.issue(rs, region(2), row_of(2), w4);
-        wait_loads<dt::kWaveLoads>();
+        dma.issue(rs, region(3), row_of(3), w4);
+        wait_loads<2 * dt::kWaveLoads>();  // K(0), K(1)
+        __syncthreads();
       } else {
         dma.issue(rs, region(0), row_of(0), w4);
         dma.issue(rs, region(1), row_of(1), w4);
+        __syncthreads();
+        wait_loads<dt::kWaveLoads>();  // V(0)
+        __syncthreads();               // group B runs one half-step behind
       }
-      __syncthreads();
-      if (G == 1) __syncthreads();  // group B runs one half-step behind
 
       // the loads of the matrix phase of step m, load i at k-step i
       auto loads = [&](int m) {
         return [&, m](int i) {
           if (i < dt::kWaveLoads) {
             if constexpr (G == 0) {
-              if (m == 1) dma.issue_one(rs, region(3), row_of(3), w4, i);
-              if (m >= 1) dma.issue_one(rs, region(m + 3), row_of(m + 3), w4, i);
+              if (m == 1) dma.issue_one(rs, region(4), row_of(4), w4, i);
+              if (m >= 1) dma.issue_one(rs, region(m + 4), row_of(m + 4), w4, i);
             } else {
               dma.issue_one(rs, region(m + 2), row_of(m + 2), w4, i);
             }
@@ -1293,18 +1316,29 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(Params prm) {
           }
         }
       };
+      // End of the softmax phase of step m - 1: group B's loads of V(m) have
+      // landed, and the first fragments of the matrix phase of step m are
+      // read, left in flight across the barrier that ends the half-step.
+      auto end_vector = [&](int m) {
+        if constexpr (G == 1) wait_loads<dt::kWaveLoads>();  // V(m)
+        __builtin_amdgcn_sched_barrier(0);
+        prefetch_k(m + 1);
+        prefetch_v(m - 1);
+        barrier_keep_reads();
+      };
       // Matrix phase of step m: S(m + 1) and O += P(m - 1) V(m - 1).  Every
       // wave runs the same MFMAs whatever its rows see (S of a tile past the
       // last is computed from whatever the slot holds and never used): one
-      // code path keeps O in the same registers throughout.
+      // code path keeps O in the same registers throughout.  The fragments
+      // are read in the same block as the MFMAs that use them, so they are
+      // not carried around the loop.
       auto matrix = [&](int m, f32x16 (&s_next)[2]) {
+        end_vector(m);
         __builtin_amdgcn_s_setprio(2);
-        prefetch_k(m + 1);
-        prefetch_v(m - 1);
         mfma_phase<D, true, true>(ktile(m + 1) + k_lane, vtile(m - 1) + v_lane, qf, s_next, pf,
                                   oacc, ka, va, st.lrnd, loads(m));
         __builtin_amdgcn_s_setprio(0);
-        if constexpr (G == 1) wait_loads<2 * dt::kWaveLoads>();
+        if constexpr (G == 0) wait_loads<2 * dt::kWaveLoads>();  // K(m + 2)
         __syncthreads();
       };
 
@@ -1317,37 +1351,25 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pp_kernel(Params prm) {
       mfma_phase<D, true, false>(ktile(1) + k_lane, nullptr, qf, sb[1], pf, oacc, ka, va,
                                  st.lrnd, no_loads);
       __builtin_amdgcn_s_setprio(0);
-      if constexpr (G == 1) wait_loads<2 * dt::kWaveLoads>();
+      if constexpr (G == 0) wait_loads<dt::kWaveLoads>();  // K(2)
       __syncthreads();
       vector(0, sb[0]);
-      if constexpr (G == 0) wait_loads<0>();
-      __syncthreads();
       int m = 1;
       for (;;) {
         if (m == count) break;
         matrix(m, sb[0]);  // S(m + 1), m odd
         vector(m, sb[1]);
-        if constexpr (G == 0) {
-          // K(m + 2): after step 1, whose loads of K(3) and K(4) interleave,
-          // wait for all of them
-          if (m == 1) {
-            wait_loads<0>();
-          } else {
-            wait_loads<dt::kWaveLoads>();
-          }
-        }
-        __syncthreads();
         ++m;
         if (m == count) break;
         matrix(m, sb[1]);  // S(m + 1), m even
         vector(m, sb[0]);
-        if constexpr (G == 0) wait_loads<dt::kWaveLoads>();
-        __syncthreads();
         ++m;
       }
-      // last step: O += P(count - 1) V(count - 1)
+      // last step: O += P(count - 1) V(count - 1), its first V^T fragments
+      // read at the end of the last softmax phase (the K fragments read there
+      // are not used)
+      end_vector(count);
       __builtin_amdgcn_s_setprio(2);
-      prefetch_v(count - 1);
       mfma_phase<D, false, true>(nullptr, vtile(count - 1) + v_lane, qf, sb[0], pf, oacc, ka, va,
                                  st.lrnd, no_loads);
       __builtin_amdgcn_s_setprio(0);
