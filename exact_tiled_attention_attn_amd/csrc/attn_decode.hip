@@ -50,6 +50,7 @@ using namespace dev;
 
 constexpr int kKeys = 32;       // keys per tile
 constexpr int kMaxEntries = 64;  // page-table entries per split (one per lane)
+constexpr float kTau = 8.0f;        // lazy-rescale threshold of the multi-column kernel, log2 units
 constexpr double kLastLevelCacheBytes = 256.0 * 1024 * 1024;  // MI355X Infinity Cache
 
 struct DecParams {
@@ -416,31 +417,47 @@ __global__ __launch_bounds__(64 * W) void attn_decode_split_mc_kernel(DecParams 
       for (int r = 0; r < 16; ++r)
         s[r] = (unsigned)(base + 8 * (r >> 2) + (r & 3)) < (unsigned)m_span ? s[r] : -INFINITY;
     }
-    float mx = s[0];
+    // Row max as a max3 tree; the reference max m2 moves (and O, and the
+    // lane's two partial sums, are rescaled) only when some column's tile
+    // max exceeds it by more than 2^kTau: the weights stay below 2^kTau, and
+    // O, l and l~ carry the same reference, so the result is unchanged up to
+    // rounding.  The sums are per lane, in independent chains, and are
+    // combined with the partner lane (the column's other 16 keys) at the end.
+    const float q0 = fmaxf(fmaxf(s[0], s[1]), s[2]), q1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
+    const float q2 = fmaxf(fmaxf(s[6], s[7]), s[8]), q3 = fmaxf(fmaxf(s[9], s[10]), s[11]);
+    const float q4 = fmaxf(fmaxf(s[12], s[13]), s[14]);
+    const float mx = wave_max_pair(fmaxf(fmaxf(fmaxf(q0, q1), q2), fmaxf(fmaxf(q3, q4), s[15]))) * c;
+    if (__builtin_amdgcn_ballot_w64(mx > m2 + kTau) != 0) {
+      const float mnew = fmaxf(m2, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+      lsum *= alpha;
+      lrnd *= alpha;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    mx = wave_max_pair(mx) * c;
-    const float mnew = fmaxf(m2, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
-    m2 = mnew;
+      for (int db = 0; db < st::kDB; ++db) oacc[db] *= alpha;
+      m2 = mnew;
+    }
     bf16x8 pf[2];
-    float ps = 0.0f, pr = 0.0f;
+    float p[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -mnew));
-      ps += p;
-      pf[r >> 3][r & 7] = (__bf16)p;
+      p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -m2));
+      pf[r >> 3][r & 7] = (__bf16)p[r];
+    }
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x2 a = {pf[i >> 1][4 * (i & 1)], pf[i >> 1][4 * (i & 1) + 1]};
+      const bf16x2 b2 = {pf[i >> 1][4 * (i & 1) + 2], pf[i >> 1][4 * (i & 1) + 3]};
+      pr[i] = __builtin_amdgcn_fdot2_f32_bf16(b2, ones, __builtin_amdgcn_fdot2_f32_bf16(a, ones, 0.0f, false), false);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bf16x2 pair = {pf[i >> 2][2 * (i & 3)], pf[i >> 2][2 * (i & 3) + 1]};
-      pr = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, pr, false);
-    }
-    lsum = lsum * alpha + wave_sum_pair(ps);
-    lrnd = lrnd * alpha + wave_sum_pair(pr);
+    for (int r = 0; r < 8; ++r) p[r] += p[r + 8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] += p[r + 4];
+    lsum += (p[0] + p[1]) + (p[2] + p[3]);
+    lrnd += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 #pragma unroll
     for (int db = 0; db < st::kDB; ++db) {
-      oacc[db] *= alpha;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -474,6 +491,8 @@ __global__ __launch_bounds__(64 * W) void attn_decode_split_mc_kernel(DecParams 
     __syncthreads();
   }
 
+  lsum = wave_sum_pair(lsum);
+  lrnd = wave_sum_pair(lrnd);
   const bool any = lsum > 0.0f;
   const float lse_s = any ? (m2 + __log2f(lsum)) * kLn2 : -INFINITY;
   const float inv = any ? 1.0f / lrnd : 0.0f;
