@@ -85,7 +85,7 @@ using dev::tile_slot;
 using dev::TileSlot;
 
 constexpr int kBN = 64;              // keys per tile
-constexpr float kTau = 8.0f;         // lazy-rescale threshold, log2 units
+constexpr float kTau = 16.0f;        // lazy-rescale threshold, log2 units
 
 struct Params {
   const uint16_t *q, *k, *v;
