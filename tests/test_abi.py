@@ -299,6 +299,34 @@ def test_decode_workspace_size(lib):
     assert n16 // ((64 + 1) * 4) >= (1 << 20) // (64 * 16)
 
 
+@pytest.mark.parametrize("args,splits", [
+    # 8 x 64/8 heads to 128k, pages of 64: 64 (sequence, KV head) groups, about
+    # 4096 single-wave workgroups -> 64 splits of 2048 keys
+    ((8, 64, 8, 1, 128, 64, 131072), 64),
+    # 32 x 32 heads to 8k, pages of 16: the 64-entry page-table limit caps a
+    # split at 1024 keys -> 8 splits
+    ((32, 32, 32, 1, 128, 16, 8192), 8),
+    # multi-query 8 x 64/1 heads to 128k: two 32-column blocks, splits of at
+    # least 1024 keys (the measured best) -> 128 splits
+    ((8, 64, 1, 1, 128, 64, 131072), 128),
+    # 8 x 32/2 heads x 4 new tokens: 64 columns, 1024-key splits -> 128
+    ((8, 32, 2, 4, 128, 64, 131072), 128),
+])
+def test_decode_split_plan_of_the_measured_workloads(lib, args, splits):
+    """The split plan behind the decode workspace, worked out by hand: one
+    partial O (d floats) and lse per (sequence, KV head, split, column)."""
+    B, Hq, Hkv, T, d = args[:5]
+    assert attn.attn_decode_workspace_size(*args) == B * Hkv * splits * (Hq // Hkv * T) * (d + 1) * 4
+
+
+def test_decode_split_plan_with_a_window(lib):
+    # window 4096, 4 new tokens, pages of 256: the span is the window plus the
+    # new tokens plus one page of rounding (4355 keys); 64 groups want 64
+    # splits, rounded up to whole pages: 18 splits of 256 keys
+    assert attn.attn_decode_workspace_size(8, 64, 8, 4, 128, 256, 131072, 4096) == \
+        8 * 8 * 18 * 32 * 129 * 4
+
+
 VAR_GOOD = dict(q=P, k=P, v=P, o=P, lse=P, cu_seqlens=P, B=2, max_seqlen=64, total_rows=100, Hq=4,
                 Hkv=2, d=128, scale=0.1, causal=0, window=0, radius=16, n_global=2)
 
